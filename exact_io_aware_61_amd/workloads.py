@@ -1,0 +1,116 @@
+"""Seeded synthetic inputs for exact attention: the five workloads and their generators.
+
+This module draws random numbers and nothing else: it holds none of the
+attention arithmetic. Both the HIP path and the CPU oracle receive the arrays
+it returns, so the two never disagree about their inputs.
+
+Workloads (shapes follow the tiled-attention description: Q, K, V are N x d per
+(batch, head); the block mask works at 128 x 128 granularity, as block-sparse
+attention on page 1, "Block-Sparse FlashAttention", keeps or drops whole blocks):
+
+  tiny      B=1 H=2  N=256   d=64  dense
+  dense2k   B=8 H=16 N=2048  d=64  dense
+  causal8k  B=2 H=16 N=8192  d=128 causal (query i sees keys j <= i)
+  causal32k B=1 H=8  N=32768 d=128 causal
+  sparse16k B=4 H=16 N=16384 d=64  128x128 block mask, off-diagonal blocks kept
+                                   with probability 0.25, diagonal always kept
+
+Recipe: one numpy PCG64 generator per workload, seeded 1000 + index (index 1..5
+in the order above); Q, K, V, dO are drawn in that order as float32 N(0, 1)
+of shape [B, H, N, d] and rounded to bfloat16 (round-to-nearest-even, torch's
+conversion). scale = float32(1/sqrt(d)). The block mask uses its own generator
+seeded 1000 + index + 1: uniform [0, 1) draws < p over an [N/128, N/128] grid,
+then the diagonal set to 1; one mask shared by every (batch, head).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+BLOCK = 128  # block-mask granularity (rows and columns)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int          # 1-based position in the workload list; seeds derive from it
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool = False
+    block_keep: float | None = None   # None = no block mask
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+    @property
+    def scale(self) -> float:
+        """float32(1/sqrt(d)), returned as the Python float of that float32."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 1, 2, 256, 64),
+    "dense2k": Workload("dense2k", 2, 8, 16, 2048, 64),
+    "causal8k": Workload("causal8k", 3, 2, 16, 8192, 128, causal=True),
+    "causal32k": Workload("causal32k", 4, 1, 8, 32768, 128, causal=True),
+    "sparse16k": Workload("sparse16k", 5, 4, 16, 16384, 64, block_keep=0.25),
+}
+
+
+def bf16_normal(rng: np.random.Generator, shape) -> torch.Tensor:
+    """float32 N(0,1) draws rounded to bfloat16 (RNE); returned as a CPU bf16 tensor."""
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+def make_qkv(B: int, H: int, N: int, d: int, seed: int, with_do: bool = True):
+    """Q, K, V (and dO) as CPU bf16 tensors [B, H, N, d], drawn in that order."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    q = bf16_normal(rng, shape)
+    k = bf16_normal(rng, shape)
+    v = bf16_normal(rng, shape)
+    do = bf16_normal(rng, shape) if with_do else None
+    return q, k, v, do
+
+
+def make_block_mask(N: int, keep: float, seed: int, block: int = BLOCK) -> np.ndarray:
+    """uint8 [N/block, N/block]: 1 = keep. Bernoulli(keep) off the diagonal, diagonal kept."""
+    nb = N // block
+    rng = np.random.default_rng(seed)
+    m = (rng.random((nb, nb)) < keep).astype(np.uint8)
+    np.fill_diagonal(m, 1)
+    return m
+
+
+def make_inputs(w: Workload, with_do: bool = True):
+    """(q, k, v, do, block_mask-or-None) for a workload, all on the CPU."""
+    q, k, v, do = make_qkv(w.B, w.H, w.N, w.d, w.seed, with_do)
+    mask = None
+    if w.block_keep is not None:
+        mask = make_block_mask(w.N, w.block_keep, w.seed + 1)
+    return q, k, v, do, mask
+
+
+def kept_fraction(N: int, causal: bool, block_mask: np.ndarray | None, block: int = BLOCK) -> float:
+    """Fraction rho of (query, key) pairs that are attended (counting, no attention math).
+
+    Used for the algorithmic FLOP count 4*B*H*N^2*d*rho.
+    """
+    if block_mask is None:
+        return (N + 1) / (2 * N) if causal else 1.0
+    nb = N // block
+    if not causal:
+        return float(block_mask.astype(np.int64).sum()) / (nb * nb)
+    # causal AND block: kept off-diagonal blocks below the diagonal are full,
+    # diagonal blocks are lower triangles of block*(block+1)/2 pairs
+    m = block_mask.astype(np.int64)
+    below = np.tril(m, -1).sum() * block * block
+    diag = np.trace(m) * block * (block + 1) // 2
+    return float(below + diag) / (N * N)
