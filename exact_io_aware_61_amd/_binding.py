@@ -1,0 +1,201 @@
+"""ctypes binding of libfa.so (include/fa.h). Argument marshalling only.
+
+Every computation runs in the library's HIP kernels; PyTorch provides device
+memory (output and workspace tensors) and the current stream. There is no
+fallback: if the library is missing or the device is not a GPU, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_MASK_CAUSAL = 1
+FA_MASK_BLOCK = 2
+MASK_BLOCK_SIZE = 128
+
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess", "fa_bwd_main",
+           "fa_bwd_finish", "fa_strerror")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"fa status {status}: {msg}")
+        self.status = status
+
+
+class FaMask(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("blocks", ctypes.c_void_p), ("bh_stride", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_61_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    mp = ctypes.POINTER(FaMask)
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp]
+    lib.fa_bwd_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp,
+                           sz, vp]
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, i32, i32, i32, i32, vp, sz, vp]
+    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz,
+                                vp]
+    lib.fa_bwd_finish.argtypes = [vp, i32, i32, i32, i32, f32, vp, sz, vp]
+    for name in EXPORTS[:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    lib.fa_strerror.argtypes = [ctypes.c_int]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load().fa_strerror(status).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise FaError(status, strerror(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _shape(q: torch.Tensor, *others):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    for t in (q,) + others:
+        if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("q, k, v (and o, dO) must be contiguous bf16 tensors of one shape")
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("tensors must live on the same GPU")
+    return tuple(int(x) for x in q.shape)
+
+
+def _mask(causal: bool, block_mask, B: int, H: int, N: int, device):
+    """Build the fa_mask_t (or None) and keep the grid tensor alive alongside it."""
+    kind = FA_MASK_CAUSAL if causal else 0
+    grid = None
+    stride = 0
+    if block_mask is not None:
+        nb = -(-N // MASK_BLOCK_SIZE)
+        grid = torch.as_tensor(block_mask).to(device=device, dtype=torch.uint8).contiguous()
+        if grid.shape == (nb, nb):
+            stride = 0
+        elif grid.shape == (B, H, nb, nb):
+            stride = nb * nb
+        else:
+            raise ValueError(f"block_mask must be [{nb}, {nb}] or [B, H, {nb}, {nb}]")
+        kind |= FA_MASK_BLOCK
+    if kind == 0:
+        return None, None
+    m = FaMask(kind, MASK_BLOCK_SIZE, None if grid is None else grid.data_ptr(), stride)
+    return ctypes.byref(m), (m, grid)
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def forward(q, k, v, *, causal: bool = False, block_mask=None, scale: float | None = None,
+            out=None, lse=None):
+    """(o, lse) = attention forward. q, k, v: [B, H, N, d] bf16 on one GPU."""
+    B, H, N, d = _shape(q, k, v)
+    scale = default_scale(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
+    mptr, keep = _mask(causal, block_mask, B, H, N, q.device)
+    _check(load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, scale, mptr,
+                         _stream(q)))
+    del keep
+    return o, lse
+
+
+def bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().fa_bwd_workspace_size(B, H, N, d, ctypes.byref(n)))
+    return int(n.value)
+
+
+def workspace(q: torch.Tensor) -> torch.Tensor:
+    B, H, N, d = (int(x) for x in q.shape)
+    return torch.empty(max(bwd_workspace_size(B, H, N, d), 16), device=q.device, dtype=torch.uint8)
+
+
+def backward(q, k, v, o, lse, do, *, causal: bool = False, block_mask=None,
+             scale: float | None = None, ws=None, dq=None, dk=None, dv=None):
+    """(dq, dk, dv) for upstream gradient do, recomputing P from lse."""
+    B, H, N, d = _shape(q, k, v, o, do)
+    scale = default_scale(d) if scale is None else float(scale)
+    ws = workspace(q) if ws is None else ws
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    mptr, keep = _mask(causal, block_mask, B, H, N, q.device)
+    _check(load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                         _ptr(dk), _ptr(dv), B, H, N, d, scale, mptr, _ptr(ws), ws.numel(),
+                         _stream(q)))
+    del keep
+    return dq, dk, dv
+
+
+def bwd_preprocess(o, do, ws):
+    B, H, N, d = _shape(o, do)
+    _check(load().fa_bwd_preprocess(_ptr(o), _ptr(do), B, H, N, d, _ptr(ws), ws.numel(),
+                                    _stream(o)))
+
+
+def bwd_main(q, k, v, do, lse, dk, dv, ws, *, causal=False, block_mask=None, scale=None):
+    B, H, N, d = _shape(q, k, v, do)
+    scale = default_scale(d) if scale is None else float(scale)
+    mptr, keep = _mask(causal, block_mask, B, H, N, q.device)
+    _check(load().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv),
+                              B, H, N, d, scale, mptr, _ptr(ws), ws.numel(), _stream(q)))
+    del keep
+
+
+def bwd_finish(dq, ws, *, scale=None):
+    B, H, N, d = (int(x) for x in dq.shape)
+    scale = default_scale(d) if scale is None else float(scale)
+    _check(load().fa_bwd_finish(_ptr(dq), B, H, N, d, scale, _ptr(ws), ws.numel(), _stream(dq)))
+
+
+class _AttentionFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, causal, block_mask, scale):
+        o, lse = forward(q, k, v, causal=causal, block_mask=block_mask, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.args = (causal, block_mask, scale)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        causal, block_mask, scale = ctx.args
+        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), causal=causal,
+                              block_mask=block_mask, scale=scale)
+        return dq, dk, dv, None, None, None
+
+
+def attention(q, k, v, *, causal: bool = False, block_mask=None, scale: float | None = None):
+    """Differentiable O = softmax(scale Q K^T, masked) V through the HIP kernels."""
+    return _AttentionFn.apply(q, k, v, causal, block_mask, scale)

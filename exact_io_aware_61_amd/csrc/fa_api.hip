@@ -1,0 +1,253 @@
+// C ABI of the attention library (declared in include/fa.h): host-side argument
+// checks, workspace layout, and kernel dispatch on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_kernels.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+struct Shape {
+  int B, H, N, d;
+  int64_t bh() const { return (int64_t)B * H; }
+  int64_t elems() const { return bh() * N * d; }
+  bool empty() const { return B == 0 || H == 0 || N == 0; }
+};
+
+int check_shape(const Shape& s) {
+  if (s.B < 0 || s.H < 0 || s.N < 0) return FA_ERR_SHAPE;
+  if (s.d != 64 && s.d != 128) return FA_ERR_SHAPE;
+  if (s.bh() > INT32_MAX) return FA_ERR_SHAPE;
+  if (s.elems() >= kMaxElems) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_scale(float scale) {
+  return (isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_SCALE;
+}
+
+// Mask check. On success fills the kernel-side description.
+int check_mask(const fa_mask_t* m, const Shape& s, fa::MaskArgs* out) {
+  out->causal = false;
+  out->blocks = nullptr;
+  out->bh_stride = 0;
+  out->nb = (s.N + 127) / 128;
+  if (m == nullptr) return FA_OK;
+  if (m->kind & ~(FA_MASK_CAUSAL | FA_MASK_BLOCK)) return FA_ERR_MASK;
+  out->causal = (m->kind & FA_MASK_CAUSAL) != 0;
+  if (m->kind & FA_MASK_BLOCK) {
+    if (m->block != 128 || m->blocks == nullptr || m->bh_stride < 0) return FA_ERR_MASK;
+    out->blocks = m->blocks;
+    out->bh_stride = m->bh_stride;
+  }
+  return FA_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + (uintptr_t)bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool any_overlap(const Range* outs, int n_out, const Range* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace layout: [D_i float32 x BH*N | pad to 256 | dQ accumulator float32 x BH*N*d].
+size_t workspace_bytes(const Shape& s) {
+  return round256((size_t)s.bh() * s.N * sizeof(float)) +
+         round256((size_t)s.elems() * sizeof(float));
+}
+
+int check_workspace(const void* ws, size_t bytes, const Shape& s) {
+  if (ws == nullptr) return FA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return FA_ERR_ALIGN;
+  if (bytes < workspace_bytes(s)) return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+void split_workspace(void* ws, const Shape& s, float** dvec, float** dqacc) {
+  char* base = static_cast<char*>(ws);
+  *dvec = reinterpret_cast<float*>(base);
+  *dqacc = reinterpret_cast<float*>(base + round256((size_t)s.bh() * s.N * sizeof(float)));
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+#define FA_TRY(expr)          \
+  do {                        \
+    const int rc_ = (expr);   \
+    if (rc_ != FA_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "unsupported shape: need B, H, N >= 0, d in {64, 128}, B*H*N*d < 2^40";
+    case FA_ERR_MASK: return "invalid mask: unknown kind, block != 128, or missing block grid";
+    case FA_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "backward workspace missing or smaller than fa_bwd_workspace_size()";
+    case FA_ERR_HIP: return "HIP runtime error at kernel launch";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_ALIAS: return "an output buffer overlaps another argument buffer";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, const fa_mask_t* mask, void* stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(check_shape(s));
+  FA_TRY(check_scale(scale));
+  fa::MaskArgs m;
+  FA_TRY(check_mask(mask, s, &m));
+  if (s.empty()) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_ALIGN;
+  const int64_t tb = s.elems() * 2;
+  const Range ins[3] = {range(q, tb), range(k, tb), range(v, tb)};
+  const Range outs[2] = {range(o, tb), range(lse, s.bh() * N * 4)};
+  if (any_overlap(outs, 2, ins, 3)) return FA_ERR_ALIAS;
+  fa::FwdArgs a{q, k, v, o, lse, (int)s.bh(), N, d, scale, m};
+  return launched(fa::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes) {
+  if (bytes == nullptr) return FA_ERR_NULL;
+  const Shape s{B, H, N, d};
+  FA_TRY(check_shape(s));
+  *bytes = workspace_bytes(s);
+  return FA_OK;
+}
+
+int fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(check_shape(s));
+  if (s.empty()) return FA_OK;
+  if (!o || !dout) return FA_ERR_NULL;
+  if (!aligned16(o) || !aligned16(dout)) return FA_ERR_ALIGN;
+  FA_TRY(check_workspace(workspace, ws_bytes, s));
+  const int64_t tb = s.elems() * 2;
+  const Range ins[2] = {range(o, tb), range(dout, tb)};
+  const Range outs[1] = {range(workspace, (int64_t)workspace_bytes(s))};
+  if (any_overlap(outs, 1, ins, 2)) return FA_ERR_ALIAS;
+  fa::BwdArgs a{};
+  a.o = o;
+  a.dout = dout;
+  a.BH = (int)s.bh();
+  a.N = N;
+  a.d = d;
+  split_workspace(workspace, s, &a.dvec, &a.dqacc);
+  return launched(fa::launch_bwd_preprocess(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                void* dk, void* dv, int B, int H, int N, int d, float scale,
+                const fa_mask_t* mask, void* workspace, size_t ws_bytes, void* stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(check_shape(s));
+  FA_TRY(check_scale(scale));
+  fa::MaskArgs m;
+  FA_TRY(check_mask(mask, s, &m));
+  if (s.empty()) return FA_OK;
+  if (!q || !k || !v || !dout || !lse || !dk || !dv) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned4(lse) ||
+      !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGN;
+  FA_TRY(check_workspace(workspace, ws_bytes, s));
+  const int64_t tb = s.elems() * 2;
+  const Range ins[5] = {range(q, tb), range(k, tb), range(v, tb), range(dout, tb),
+                        range(lse, s.bh() * N * 4)};
+  const Range outs[3] = {range(dk, tb), range(dv, tb),
+                         range(workspace, (int64_t)workspace_bytes(s))};
+  if (any_overlap(outs, 3, ins, 5)) return FA_ERR_ALIAS;
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.dk = dk;
+  a.dv = dv;
+  a.BH = (int)s.bh();
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.mask = m;
+  split_workspace(workspace, s, &a.dvec, &a.dqacc);
+  return launched(fa::launch_bwd_main(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_finish(void* dq, int B, int H, int N, int d, float scale, void* workspace,
+                  size_t ws_bytes, void* stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(check_shape(s));
+  FA_TRY(check_scale(scale));
+  if (s.empty()) return FA_OK;
+  if (!dq) return FA_ERR_NULL;
+  if (!aligned16(dq)) return FA_ERR_ALIGN;
+  FA_TRY(check_workspace(workspace, ws_bytes, s));
+  const Range ins[1] = {range(workspace, (int64_t)workspace_bytes(s))};
+  const Range outs[1] = {range(dq, s.elems() * 2)};
+  if (any_overlap(outs, 1, ins, 1)) return FA_ERR_ALIAS;
+  fa::BwdArgs a{};
+  a.dq = dq;
+  a.BH = (int)s.bh();
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  split_workspace(workspace, s, &a.dvec, &a.dqacc);
+  return launched(fa::launch_bwd_finish(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+           float scale, const fa_mask_t* mask, void* workspace, size_t ws_bytes, void* stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(check_shape(s));
+  FA_TRY(check_scale(scale));
+  fa::MaskArgs m;
+  FA_TRY(check_mask(mask, s, &m));
+  if (s.empty()) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned4(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGN;
+  FA_TRY(check_workspace(workspace, ws_bytes, s));
+  const int64_t tb = s.elems() * 2;
+  const Range ins[6] = {range(q, tb), range(k, tb), range(v, tb), range(o, tb), range(dout, tb),
+                        range(lse, s.bh() * N * 4)};
+  const Range outs[4] = {range(dq, tb), range(dk, tb), range(dv, tb),
+                         range(workspace, (int64_t)workspace_bytes(s))};
+  if (any_overlap(outs, 4, ins, 6)) return FA_ERR_ALIAS;
+  FA_TRY(fa_bwd_preprocess(o, dout, B, H, N, d, workspace, ws_bytes, stream));
+  FA_TRY(fa_bwd_main(q, k, v, dout, lse, dk, dv, B, H, N, d, scale, mask, workspace, ws_bytes,
+                     stream));
+  return fa_bwd_finish(dq, B, H, N, d, scale, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Shared device helpers for the gfx950 attention kernels: vector types, bf16 MFMA,
+// LDS reads (plain and transposing), packing. CDNA4 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
+// Lane l supplies A row (l % 32), k = 8*(l/32) .. +7, and B column (l % 32), same k.
+// Lane l receives D column (l % 32), rows 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16 contiguous bytes from LDS.
+__device__ __forceinline__ bf16x8 lds_b128(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, lane i
+// points at 4 consecutive bf16 of a row-major tile; lane j gets back element e
+// = the (j%4)-th element of lane (4e + j/4)'s four. Point lane i at
+// tile[r0 + i/4][c0 + 4*(i%4)] and lane j receives tile[r0 .. r0+3][c0 + j]:
+// one column, four consecutive rows.
+__device__ __forceinline__ i16x4 lds_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_char*)p));
+}
+
+__device__ __forceinline__ bf16x8 cat(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Eight fp32 -> eight bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3, float a4,
+                                            float a5, float a6, float a7) {
+  f32x8 x = {a0, a1, a2, a3, a4, a5, a6, a7};
+  return __builtin_convertvector(x, bf16x8);
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(float a0, float a1, float a2, float a3) {
+  f32x4 x = {a0, a1, a2, a3};
+  return __builtin_convertvector(x, bf16x4);
+}
+
+// Exchange with the lane 32 away (the other half of the wave).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+}  // namespace fa

@@ -1,0 +1,297 @@
+// Forward attention for gfx950: O = softmax(scale Q K^T, masked) V and LSE.
+//
+// Follows the tiled forward with the online softmax (lecture summary on
+// FlashAttention v1, sections 3.1-3.3) in the FlashAttention-2 loop order
+// (FlashAttention-2 overview, forward pass): each workgroup owns one block of
+// query rows of one (batch, head) and sweeps the key/value tiles, so no
+// workgroup talks to another. Inside the workgroup every wave owns 32 query
+// rows (the "split-Q" partition of the same overview): K/V tiles are shared
+// through LDS, and no partial results are exchanged between waves.
+//
+// Per wave and K/V tile (BN keys):
+//   S^T = K_tile Q_wave^T       MFMA 32x32x16, K read from LDS, Q^T held in VGPRs.
+//                               The transposed product puts one query row in each
+//                               lane (the same row in lanes l and l+32), so a row
+//                               max is a lane-local max plus one cross-half swap.
+//   m' = max(m, rowmax S^T * scale*log2e); alpha = 2^(m - m');
+//   P^T = 2^(S^T * scale*log2e - m');  l = alpha l + rowsum P^T  (per lane half)
+//   O^T = alpha O^T + V_tile^T P^T  MFMA, P^T straight from registers as the B
+//                               operand; V^T via the transposing LDS read.
+// Normalisation by l happens once at the end (the reading of the
+// FlashAttention-2 "fewer non-matmul operations" change), and
+// LSE = ln2 * (m + log2 l) is written instead of (m, l).
+#include "fa_common.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+namespace {
+
+template <int D>
+struct FwdCfg {
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BM = 32 * WAVES;           // query rows per workgroup
+  static constexpr int BN = 64;                   // keys per K/V tile
+  // LDS row stride in bf16 elements: 76 dwords (d=128) / 36 dwords (d=64), so
+  // 16-byte row reads of 16 consecutive rows and the transposing reads of 4
+  // consecutive rows fall in distinct banks.
+  static constexpr int STR = D == 128 ? 152 : 72;
+  static constexpr int KS = D / 16;               // MFMA k-steps over the head dim
+  static constexpr int NT = BN / 32;              // 32-key sub-tiles of S^T
+  static constexpr int CT = D / 32;               // 32-column sub-tiles of O^T
+  static constexpr int CHUNKS = BN * D / 8;       // 16-byte pieces per K or V tile
+  static constexpr int CPT = CHUNKS / THREADS;    // ... per thread
+  static constexpr int TILE = BN * STR;           // elements per LDS tile
+  static_assert(CHUNKS % THREADS == 0, "tile must split evenly over threads");
+};
+
+struct FwdParams {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  int BH;
+  int N;
+  int n_row_blocks;
+  float sl2;  // scale * log2(e)
+  const uint8_t* blocks;
+  int64_t blocks_bh_stride;
+  int nb;
+};
+
+template <int D, bool CAUSAL, bool BLOCK>
+__global__ __launch_bounds__(256) void fa_fwd_kernel(FwdParams p) {
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * C::TILE];  // [buffer][K, V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;     // which half of the wave
+  const int g16 = lane >> 4;    // 16-lane group (transposing reads)
+  const int i16 = lane & 15;
+
+  // Largest row blocks first: under a causal mask they carry the most tiles.
+  const int bh = blockIdx.x % p.BH;
+  const int rb = p.n_row_blocks - 1 - blockIdx.x / p.BH;
+  const int N = p.N;
+  const int64_t head = (int64_t)bh * N * D;
+  const bf16* __restrict__ Qh = p.q + head;
+  const bf16* __restrict__ Kh = p.k + head;
+  const bf16* __restrict__ Vh = p.v + head;
+  const int row0 = rb * C::BM;
+  const int wrow0 = row0 + 32 * wave;   // first row of this wave
+  const int qrow = wrow0 + l32;         // this lane's query row
+
+  int kt_end = (N + C::BN - 1) / C::BN;
+  if (CAUSAL) kt_end = min(kt_end, (row0 + C::BM - 1) / C::BN + 1);
+  const uint8_t* mrow = nullptr;
+  if (BLOCK) mrow = p.blocks + bh * p.blocks_bh_stride + (int64_t)(row0 / 128) * p.nb;
+  auto kept = [&](int kt) -> bool { return !BLOCK || mrow[(kt * C::BN) / 128] != 0; };
+  auto next_kept = [&](int kt) -> int {
+    ++kt;
+    while (kt < kt_end && !kept(kt)) ++kt;
+    return kt;
+  };
+
+  // Q^T operand: lane holds Q[qrow][16*kk + 8*hh .. +7] for every k-step.
+  bf16x8 qf[C::KS];
+#pragma unroll
+  for (int kk = 0; kk < C::KS; ++kk) {
+    if (qrow < N)
+      qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qrow * D + 16 * kk + 8 * hh);
+    else
+      qf[kk] = bf16x8{};
+  }
+
+  u32x4 kst[C::CPT], vst[C::CPT];  // staging registers for the next tile
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int c = 0; c < C::CPT; ++c) {
+      const int id = tid + c * C::THREADS;
+      const int r = id / (D / 8);
+      const int col = (id % (D / 8)) * 8;
+      const int key = kt * C::BN + r;
+      if (key < N) {
+        kst[c] = *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + col);
+        vst[c] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + col);
+      } else {
+        kst[c] = u32x4{0, 0, 0, 0};
+        vst[c] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    bf16* Ks = smem + buf * 2 * C::TILE;
+    bf16* Vs = Ks + C::TILE;
+#pragma unroll
+    for (int c = 0; c < C::CPT; ++c) {
+      const int id = tid + c * C::THREADS;
+      const int r = id / (D / 8);
+      const int col = (id % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(Ks + r * C::STR + col) = kst[c];
+      *reinterpret_cast<u32x4*>(Vs + r * C::STR + col) = vst[c];
+    }
+  };
+
+  f32x16 oacc[C::CT];
+#pragma unroll
+  for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = f32x16{};
+  float m_run = -INFINITY;  // running max of scaled scores, log2 domain
+  float l_run = 0.f;        // running denominator, this lane half's keys only
+
+  auto compute = [&](int kt, int buf) {
+    const bf16* Ks = smem + buf * 2 * C::TILE;
+    const bf16* Vs = Ks + C::TILE;
+    const int kbase = kt * C::BN;
+    // Under the causal mask a wave whose rows all precede this tile sees none of it.
+    if (CAUSAL && kbase > wrow0 + 31) return;
+
+    f32x16 s[C::NT];
+#pragma unroll
+    for (int st = 0; st < C::NT; ++st) s[st] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk) {
+#pragma unroll
+      for (int st = 0; st < C::NT; ++st) {
+        const bf16x8 a = lds_b128(Ks + (32 * st + l32) * C::STR + 16 * kk + 8 * hh);
+        s[st] = mfma32(a, qf[kk], s[st]);
+      }
+    }
+    // s[st][v] is the score of query qrow and key kbase + 32*st + 8*(v/4) + 4*hh + v%4.
+    const bool edge = (CAUSAL && kbase + C::BN - 1 > wrow0) || (kbase + C::BN > N);
+    if (edge) {
+#pragma unroll
+      for (int st = 0; st < C::NT; ++st) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kbase + 32 * st + 8 * (v / 4) + 4 * hh + (v % 4);
+          if ((CAUSAL && key > qrow) || key >= N) s[st][v] = -INFINITY;
+        }
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < C::NT; ++st) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[st][v]);
+    }
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_new = fmaxf(m_run, mx * p.sl2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // a row with nothing visible yet
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+
+    bf16x8 pk[2 * C::NT];
+    float rs = 0.f;
+#pragma unroll
+    for (int st = 0; st < C::NT; ++st) {
+      float e[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        e[v] = fast_exp2(__builtin_fmaf(s[st][v], p.sl2, -m_use));
+        rs += e[v];
+      }
+      pk[2 * st] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      pk[2 * st + 1] = to_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+    }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) oacc[ct] *= alpha;
+
+    // O^T[c][i] += sum_j V[j][c] P^T[j][i]. MFMA k-slot order within each 16 keys
+    // follows the accumulator layout of S^T: lane half hh holds keys 4hh..4hh+3 and
+    // 8+4hh..8+4hh+3, so the V^T operand is read as those two groups of four rows.
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) {
+      const int n0 = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
+#pragma unroll
+      for (int ks = 0; ks < 2 * C::NT; ++ks) {
+        const int r0 = 16 * ks + 4 * hh + (i16 >> 2);
+        const i16x4 lo = lds_tr(Vs + r0 * C::STR + n0);
+        const i16x4 hi = lds_tr(Vs + (r0 + 8) * C::STR + n0);
+        oacc[ct] = mfma32(cat(lo, hi), pk[ks], oacc[ct]);
+      }
+    }
+  };
+
+  int kt = 0;
+  if (BLOCK && kt < kt_end && !kept(kt)) kt = next_kept(kt);
+  if (kt < kt_end) {
+    load_tile(kt);
+    store_tile(0);
+    __syncthreads();
+    int buf = 0;
+    while (kt < kt_end) {
+      const int kn = next_kept(kt);
+      if (kn < kt_end) load_tile(kn);
+      compute(kt, buf);
+      if (kn < kt_end) store_tile(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+      kt = kn;
+    }
+  }
+
+  // Epilogue: combine the two lane halves' denominators, normalise once.
+  const float l_tot = l_run + swap_halves(l_run);
+  const float inv = l_tot > 0.f ? fast_rcp(l_tot) : 0.f;
+  if (qrow < N) {
+    bf16* orow = p.o + head + (int64_t)qrow * D;
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 32 * ct + 8 * g + 4 * hh;
+        *reinterpret_cast<bf16x4*>(orow + c) =
+            to_bf16x4(oacc[ct][4 * g] * inv, oacc[ct][4 * g + 1] * inv,
+                      oacc[ct][4 * g + 2] * inv, oacc[ct][4 * g + 3] * inv);
+      }
+    }
+    if (hh == 0)
+      p.lse[(int64_t)bh * N + qrow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  FwdParams p;
+  p.q = static_cast<const bf16*>(a.q);
+  p.k = static_cast<const bf16*>(a.k);
+  p.v = static_cast<const bf16*>(a.v);
+  p.o = static_cast<bf16*>(a.o);
+  p.lse = a.lse;
+  p.BH = a.BH;
+  p.N = a.N;
+  p.n_row_blocks = (a.N + C::BM - 1) / C::BM;
+  p.sl2 = a.scale * kLog2e;
+  p.blocks = a.mask.blocks;
+  p.blocks_bh_stride = a.mask.bh_stride;
+  p.nb = a.mask.nb;
+  const dim3 grid((unsigned)p.n_row_blocks * (unsigned)a.BH);
+  const dim3 block(C::THREADS);
+  const bool blk = a.mask.blocks != nullptr;
+  if (a.mask.causal) {
+    if (blk)
+      hipLaunchKernelGGL((fa_fwd_kernel<D, true, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((fa_fwd_kernel<D, true, false>), grid, block, 0, stream, p);
+  } else {
+    if (blk)
+      hipLaunchKernelGGL((fa_fwd_kernel<D, false, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((fa_fwd_kernel<D, false, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  return a.d == 128 ? launch_d<128>(a, stream) : launch_d<64>(a, stream);
+}
+
+}  // namespace fa

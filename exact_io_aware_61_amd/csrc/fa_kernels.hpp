@@ -1,0 +1,50 @@
+// Kernel launch interface between the C ABI (fa_api.hip) and the kernel files.
+// Arguments here are already validated; launchers only pick an instantiation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct MaskArgs {
+  bool causal;
+  const uint8_t* blocks;  // nullptr = no block mask; else [nb][nb] per (b, h)
+  int64_t bh_stride;      // elements between (b, h) grids (0 = shared)
+  int nb;                 // ceil(N / 128)
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int BH, N, d;
+  float scale;
+  MaskArgs mask;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int BH, N, d;
+  float scale;
+  MaskArgs mask;
+  float* dvec;   // workspace: D_i [BH * N]
+  float* dqacc;  // workspace: fp32 dQ accumulator [BH * N * d]
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace fa

@@ -81,8 +81,9 @@ def make_qkv(B: int, H: int, N: int, d: int, seed: int, with_do: bool = True):
 
 
 def make_block_mask(N: int, keep: float, seed: int, block: int = BLOCK) -> np.ndarray:
-    """uint8 [N/block, N/block]: 1 = keep. Bernoulli(keep) off the diagonal, diagonal kept."""
-    nb = N // block
+    """uint8 [nb, nb] with nb = ceil(N/block): 1 = keep. Bernoulli(keep) off the diagonal,
+    diagonal kept."""
+    nb = -(-N // block)
     rng = np.random.default_rng(seed)
     m = (rng.random((nb, nb)) < keep).astype(np.uint8)
     np.fill_diagonal(m, 1)
@@ -105,6 +106,8 @@ def kept_fraction(N: int, causal: bool, block_mask: np.ndarray | None, block: in
     """
     if block_mask is None:
         return (N + 1) / (2 * N) if causal else 1.0
+    if N % block:
+        raise ValueError("kept_fraction counts whole mask blocks: N must be a multiple of block")
     nb = N // block
     if not causal:
         return float(block_mask.astype(np.int64).sum()) / (nb * nb)

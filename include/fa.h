@@ -1,0 +1,146 @@
+/*
+ * fa.h - exact, IO-aware attention on AMD Instinct MI355X (gfx950).
+ *
+ * Computes O = softmax(scale * Q K^T [masked]) V without ever writing the N x N
+ * score (S) or probability (P) matrices to device memory, and its gradients,
+ * which recompute P from the saved per-row logsumexp.
+ *
+ * Sources (three web pages on FlashAttention):
+ *   - lecture summary on FlashAttention v1 (spark.aweffr.cn), section 2.1: the
+ *     attention formula softmax(Q K^T / sqrt(d_k)) V; section 3.2: the one-pass
+ *     online softmax; section 3.3: the tiled forward; part 4.2: the backward
+ *     recomputes S and P from the saved statistics.
+ *   - FlashAttention-2 overview (jishu.shishitao.com), "main operations": the
+ *     backward needs only the row logsumexp; the forward gives each worker one
+ *     block of query rows; the backward gives each worker one block of key
+ *     columns and merges dQ by atomic addition; block-sparse attention skips
+ *     zero blocks ("Block-Sparse FlashAttention").
+ *
+ * Conventions shared by every entry point:
+ *   Layout     Q, K, V, O, dO, dQ, dK, dV are [B, H, N, d] bfloat16, contiguous,
+ *              d fastest. lse is [B, H, N] float32 (natural-log logsumexp of the
+ *              scaled, masked scores of each query row).
+ *   Memory     every data pointer is a DEVICE pointer owned by the caller; the
+ *              library allocates nothing and keeps no mutable global state.
+ *              Inputs are read-only; outputs must not overlap any input.
+ *   Alignment  data pointers must be 16-byte aligned.
+ *   Limits     B, H, N >= 0 (a zero extent is a no-op that returns FA_OK);
+ *              d in {64, 128}; scale finite and > 0; B*H*N*d < 2^40.
+ *              N need not be a multiple of any tile size.
+ *   Streams    `stream` is a hipStream_t passed as void* (NULL = default
+ *              stream). Every call only enqueues work and returns; results are
+ *              ready after the caller synchronises the stream. Device faults
+ *              surface at that synchronisation.
+ *   Errors     argument checks run on the host before anything is enqueued and
+ *              return a negative fa_status; nothing is written then. A failed
+ *              kernel launch returns FA_ERR_HIP.
+ *   Determinism fa_fwd, dK and dV are bitwise reproducible run to run; dQ is
+ *              merged by floating-point atomics, so its low bits may vary.
+ */
+#ifndef EXACT_IO_AWARE_FA_H
+#define EXACT_IO_AWARE_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,      /* a required pointer is NULL                            */
+  FA_ERR_SHAPE = -2,     /* B/H/N negative, d unsupported, or sizes overflow       */
+  FA_ERR_MASK = -3,      /* unknown mask kind, block != 128, or NULL block grid    */
+  FA_ERR_ALIGN = -4,     /* a data pointer is not 16-byte aligned                  */
+  FA_ERR_WORKSPACE = -5, /* backward workspace missing or too small                */
+  FA_ERR_HIP = -6,       /* the HIP runtime reported an error at launch            */
+  FA_ERR_SCALE = -7,     /* scale is not finite and > 0                            */
+  FA_ERR_ALIAS = -8      /* an output range overlaps an input range                */
+} fa_status;
+
+/* Mask kinds (bit flags; 0 = every key visible to every query). */
+#define FA_MASK_CAUSAL 1 /* query i sees key j iff j <= i                                     */
+#define FA_MASK_BLOCK 2  /* query i sees key j iff blocks[i / 128][j / 128] != 0              */
+
+/*
+ * Mask description. Block-sparse attention (FlashAttention-2 overview, section
+ * "Block-Sparse FlashAttention") keeps or drops whole blocks of the score
+ * matrix; blocks whose entry is 0 are skipped entirely and contribute exactly
+ * zero to O and to every gradient. Both flags may be combined (logical AND).
+ */
+typedef struct fa_mask {
+  int32_t kind;           /* OR of FA_MASK_* flags                                       */
+  int32_t block;          /* block edge in rows/keys; must be 128 when FA_MASK_BLOCK is set */
+  const uint8_t* blocks;  /* DEVICE pointer, uint8 [nb][nb] row-major, nb = ceil(N / 128); */
+                          /* nonzero = keep. Read-only. Ignored unless FA_MASK_BLOCK.       */
+  int64_t bh_stride;      /* elements between the grids of consecutive (b, h); 0 = one grid */
+                          /* shared by every (b, h), else grid of (b, h) at blocks + (b*H+h)*bh_stride */
+} fa_mask_t;
+
+/*
+ * Forward: O = softmax(scale * Q K^T, masked) V and lse = row logsumexp.
+ * Tiled with the online softmax (lecture summary, section 3.2; FlashAttention-2
+ * overview, forward pass): one workgroup per (b, h, block of query rows), a
+ * running max and denominator per row kept on chip, normalisation deferred to
+ * the end. A row with no visible key gets O = 0 and lse = -inf.
+ *   q, k, v : inputs [B, H, N, d] bf16
+ *   o       : output [B, H, N, d] bf16 (round-to-nearest-even)
+ *   lse     : output [B, H, N] float32, natural log
+ *   mask    : NULL = no mask
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, const fa_mask_t* mask, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: the row terms D_i = dO_i . O_i
+ * ([B, H, N] float32) and the float32 dQ accumulator ([B, H, N, d]), each
+ * 256-byte aligned. Writes the size to *bytes. Pure host arithmetic.
+ */
+int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);
+
+/*
+ * Backward: dQ, dK, dV of L given dO = dL/dO, recomputing P tile by tile from
+ * q, k and the forward's lse (lecture summary, part 4.2; FlashAttention-2
+ * overview, backward pass: one workgroup per block of key columns, dQ merged
+ * across workgroups by atomic addition).
+ *   q, k, v, o, dout : inputs [B, H, N, d] bf16 (o from fa_fwd with the same arguments)
+ *   lse              : input [B, H, N] float32 from fa_fwd
+ *   dq, dk, dv       : outputs [B, H, N, d] bf16
+ *   workspace        : DEVICE buffer of at least fa_bwd_workspace_size() bytes,
+ *                      owned by the caller; its contents on entry do not matter
+ *                      and are overwritten.
+ * Enqueues three kernels: fa_bwd_preprocess, fa_bwd_main, fa_bwd_finish (below).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, const fa_mask_t* mask,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The three stages of fa_bwd, exposed so a caller can time or schedule them
+ * separately; calling them in order on one stream equals fa_bwd.
+ *   fa_bwd_preprocess : D_i = sum_c dO_ic O_ic into the workspace, and zeroes
+ *                       the float32 dQ accumulator.
+ *   fa_bwd_main       : dK, dV (written as bf16) and dQ accumulated in float32
+ *                       in the workspace.
+ *   fa_bwd_finish     : writes dq = bf16(scale * dQ accumulator).
+ * Argument meanings and checks are those of fa_bwd.
+ */
+int fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d,
+                      void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+                const float* lse, void* dk, void* dv,
+                int B, int H, int N, int d, float scale, const fa_mask_t* mask,
+                void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_finish(void* dq, int B, int H, int N, int d, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_IO_AWARE_FA_H */
