@@ -1,0 +1,267 @@
+"""Benchmark: exact attention forward + backward through the HIP library (libfa.so).
+
+One step = one pass of the whole path on one batch of synthetic input:
+fa_fwd, then the backward's three stages (fa_bwd_preprocess, fa_bwd_main,
+fa_bwd_finish, which together are fa_bwd). Inputs, outputs and workspace are
+resident in device memory before the timed region starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload causal8k] [--cpu-seconds 10]
+
+Prints ONE JSON line. `value` is fwd+bwd throughput in TFLOP/s over the wall
+clock of the K timed steps, counting matmul FLOPs only: forward
+4*B*H*N^2*d*rho (two N x N x d products), backward 2.5x that (five products,
+the recompute of S included), rho = fraction of (query, key) pairs attended.
+`roofline` is the kernel with the largest share of the step, timed with HIP
+events recorded on the stream the kernels run on, against the dense bf16 MFMA
+peak of MI355X. `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample
+(whole heads, forward + backward) on this host's cores, with the same FLOP
+numerator per head.
+
+--probe copy runs an elementwise kernel that reads and writes a buffer of known
+size, used to calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd & fwd+bwd TFLOP/s and % of bf16 MFMA peak, N=2k–32k"
+# MI355X dense bf16 MFMA peak: 256 CU x 4096 FLOP/clk/CU x 2.4 GHz.
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_common.hpp", "fa_kernels.hpp")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="causal8k",
+                    help="tiny | dense2k | causal8k | causal32k | sparse16k")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="the CPU oracle runs whole heads until this much time has passed "
+                         "(at least one head; 0 = skip cpu_baseline)")
+    ap.add_argument("--probe", choices=["copy"], default=None)
+    ap.add_argument("--probe-mib", type=int, default=1024)
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_io_aware_61_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken on this source.
+
+    profiles/traffic_<kernel>_<workload>.md holds a line
+    `traffic-record: {"src": "<digest>", "bytes_per_launch": X, ...}`.
+    """
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic-record:"):
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("src") == digest:
+                    return rec
+    return None
+
+
+def probe_copy(mib: int, steps: int):
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.randn(n, device="cuda:0", dtype=torch.float32)
+    y = torch.empty_like(x)
+    for _ in range(steps):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n,
+                      "launches": steps}), flush=True)
+
+
+def cpu_baseline(w, q, k, v, do, bm, seconds: float):
+    """Time the oracle on whole heads (forward + backward) on the host cores.
+
+    Heads run one after another until `seconds` have passed (at least one head,
+    at most all of them); the rate is the heads done over the time they took.
+    """
+    import numpy as np
+    import threadpoolctl
+    from oracle import attention_head
+    from exact_io_aware_61_amd.workloads import kept_fraction
+
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
+                   if p.get("user_api") == "blas"] or [1])
+    done, dt = 0, 0.0
+    while done < w.B * w.H and (done == 0 or dt < seconds):
+        b, h = divmod(done, w.H)
+        qa, ka, va, da = (t[b, h].double().numpy() for t in (q, k, v, do))
+        t0 = time.perf_counter()
+        attention_head(qa, ka, va, da, scale=w.scale, causal=w.causal, block_mask=bm)
+        dt += time.perf_counter() - t0
+        done += 1
+    rho = kept_fraction(w.N, w.causal, bm)
+    flops = 3.5 * 4.0 * w.N * w.N * w.d * rho * done
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {w.B * w.H} heads of {w.name}, forward+backward, fp64 "
+                      f"NumPy with S and P materialised, {dt:.2f} s",
+            "seconds": dt, "cpu": platform.processor() or platform.machine(),
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): attention heads are independent, so a multi-GPU run would be one "
+              f"single-GPU run per head shard with no exchange between them.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_io_aware_61_amd as fa
+    from exact_io_aware_61_amd.workloads import WORKLOADS, kept_fraction, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (none visible)", file=sys.stderr)
+        sys.exit(1)
+    if args.probe == "copy":
+        probe_copy(args.probe_mib, args.steps)
+        return
+
+    lib = fa.load()
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] workload {w.name} B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} "
+          f"block_keep={w.block_keep}", file=sys.stderr, flush=True)
+    q, k, v, do, bm = make_inputs(w)
+    qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
+    o = torch.empty_like(qg)
+    lse = torch.empty((w.B, w.H, w.N), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
+    ws = fa.workspace(qg)
+    kind = fa.FA_MASK_CAUSAL if w.causal else 0
+    grid = None
+    if bm is not None:
+        grid = torch.from_numpy(bm).to(dev)
+        kind |= fa.FA_MASK_BLOCK
+    mask = None
+    if kind:
+        mask_s = fa._binding.FaMask(kind, fa.MASK_BLOCK_SIZE,
+                                    None if grid is None else grid.data_ptr(), 0)
+        mask = ctypes.byref(mask_s)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    B, H, N, d, sc = w.B, w.H, w.N, w.d, ctypes.c_float(w.scale)
+    wsn = ctypes.c_size_t(ws.numel())
+
+    def check(rc):
+        if rc != 0:
+            raise fa.FaError(rc, fa.strerror(rc))
+
+    def fwd():
+        check(lib.fa_fwd(P(qg), P(kg), P(vg), P(o), P(lse), B, H, N, d, sc, mask, sp))
+
+    def pre():
+        check(lib.fa_bwd_preprocess(P(o), P(dog), B, H, N, d, P(ws), wsn, sp))
+
+    def main_bwd():
+        check(lib.fa_bwd_main(P(qg), P(kg), P(vg), P(dog), P(lse), P(dk), P(dv), B, H, N, d, sc,
+                              mask, P(ws), wsn, sp))
+
+    def fin():
+        check(lib.fa_bwd_finish(P(dq), B, H, N, d, sc, P(ws), wsn, sp))
+
+    stages = [("fa_fwd_kernel", fwd), ("fa_bwd_pre_kernel", pre),
+              ("fa_bwd_main_kernel", main_bwd), ("fa_bwd_finish_kernel", fin)]
+
+    for i in range(args.warmup):
+        for _, f in stages:
+            f()
+        print(f"[bench] warmup step {i + 1}/{args.warmup}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        ev[s][0].record(stream)
+        for j, (_, f) in enumerate(stages):
+            f()
+            ev[s][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] timed {K} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    per = {name: float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(K)]))
+           for j, (name, _) in enumerate(stages)}
+    fwd_ms = per["fa_fwd_kernel"]
+    bwd_ms = sum(per[n] for n, _ in stages[1:])
+    rho = kept_fraction(w.N, w.causal, bm)
+    fwd_flop = 4.0 * w.B * w.H * w.N * w.N * w.d * rho
+    step_flop = 3.5 * fwd_flop
+    ms_per_step = wall / K * 1e3
+    value = step_flop / (ms_per_step * 1e-3) / 1e12
+
+    kernel_flop = {"fa_fwd_kernel": fwd_flop, "fa_bwd_main_kernel": 2.5 * fwd_flop}
+    dom = max(kernel_flop, key=lambda n: per[n])
+    achieved = kernel_flop[dom] / (per[dom] * 1e-3) / 1e12
+    digest = source_digest()
+    rec = traffic_record(dom, w.name, digest)
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None if rec is None else rec["bytes_per_launch"],
+                "avg_launch_ms": round(per[dom], 4), "flop_per_launch": kernel_flop[dom]}
+
+    fwd_tf = fwd_flop / (fwd_ms * 1e-3) / 1e12
+    fb_ms = fwd_ms + bwd_ms
+    fb_tf = step_flop / (fb_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "mask": "causal" if w.causal else ("block" if bm is not None else "none"),
+                   "block_keep": w.block_keep, "rho": round(rho, 6), "scale": w.scale},
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2),
+                "frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "fwd_bwd": {"ms": round(fb_ms, 4), "tflops": round(fb_tf, 2),
+                    "frac_of_peak": round(fb_tf / PEAK_BF16_TFLOPS, 4)},
+        "kernel_ms": {n: round(t, 4) for n, t in per.items()},
+        "roofline": roofline,
+        "src": digest,
+    }
+    if args.cpu_seconds > 0:
+        print(f"[bench] cpu baseline: oracle on whole heads for ~{args.cpu_seconds} s",
+              file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, do, bm, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
