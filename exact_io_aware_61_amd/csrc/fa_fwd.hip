@@ -13,13 +13,23 @@
 //                               The transposed product puts one query row in each
 //                               lane (the same row in lanes l and l+32), so a row
 //                               max is a lane-local max plus one cross-half swap.
-//   m' = max(m, rowmax S^T * scale*log2e); alpha = 2^(m - m');
-//   P^T = 2^(S^T * scale*log2e - m');  l = alpha l + rowsum P^T  (per lane half)
-//   O^T = alpha O^T + V_tile^T P^T  MFMA, P^T straight from registers as the B
+//   P^T = 2^(S^T * scale*log2e - m)                 (m: the row's reference max)
+//   l  += rowsum(P^T)           fp32, before P is rounded to bf16: gives the LSE
+//   lb += rowsum(bf16(P^T))     bf16 dot products: the sum of exactly the
+//                               probabilities the next product consumes, used to
+//                               normalise O (then O is a convex combination of V
+//                               rows even when one probability dominates)
+//   O^T += V_tile^T P^T         MFMA, P^T straight from registers as the B
 //                               operand; V^T via the transposing LDS read.
-// Normalisation by l happens once at the end (the reading of the
-// FlashAttention-2 "fewer non-matmul operations" change), and
-// LSE = ln2 * (m + log2 l) is written instead of (m, l).
+// The reference max m only moves when a tile's row max exceeds it by more than
+// 2^8 (in probability terms); then O^T and l are rescaled by 2^(m_old - m_new).
+// Between moves P stays below 2^8, far inside fp32/bf16 range, and because O
+// and l always share the same m the final O / l is the same exact quantity as
+// the per-tile rescaled recurrence of the lecture (section 3.2), with the
+// rescale of O skipped on almost every tile. Normalisation by l happens once
+// at the end (the reading of the FlashAttention-2 "fewer non-matmul
+// operations" change), and LSE = ln2 * (m + log2 l) is written instead of
+// (m, l).
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -32,18 +42,26 @@ struct FwdCfg {
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;           // query rows per workgroup
   static constexpr int BN = 64;                   // keys per K/V tile
-  // LDS row stride in bf16 elements: 76 dwords (d=128) / 36 dwords (d=64), so
-  // 16-byte row reads of 16 consecutive rows and the transposing reads of 4
-  // consecutive rows fall in distinct banks.
-  static constexpr int STR = D == 128 ? 152 : 72;
+  // LDS row strides in bf16 elements. K is read with 16-byte row reads of 32
+  // consecutive rows: a stride of 4 (mod 64) dwords spreads them over all 64
+  // banks. V is read with the transposing 8-byte read of 8 rows x 64 bytes: a
+  // stride of 16 (mod 64) dwords puts four consecutive rows on disjoint banks.
+  static constexpr int STRK = D + 8;              // 136 / 72
+  static constexpr int STRV = D + 32;             // 160 / 96
   static constexpr int KS = D / 16;               // MFMA k-steps over the head dim
   static constexpr int NT = BN / 32;              // 32-key sub-tiles of S^T
   static constexpr int CT = D / 32;               // 32-column sub-tiles of O^T
   static constexpr int CHUNKS = BN * D / 8;       // 16-byte pieces per K or V tile
   static constexpr int CPT = CHUNKS / THREADS;    // ... per thread
-  static constexpr int TILE = BN * STR;           // elements per LDS tile
+  static constexpr int KTILE = BN * STRK;         // elements per LDS K tile
+  static constexpr int VTILE = BN * STRV;         // elements per LDS V tile
+  static constexpr int STAGE = KTILE + VTILE;
   static_assert(CHUNKS % THREADS == 0, "tile must split evenly over threads");
 };
+
+// Reference-max moves happen only when a row max exceeds it by more than this
+// (log2 units): probabilities stay <= 2^8 between moves.
+constexpr float kRescaleThreshold = 8.0f;
 
 struct FwdParams {
   const bf16* q;
@@ -61,9 +79,10 @@ struct FwdParams {
 };
 
 template <int D, bool CAUSAL, bool BLOCK>
-__global__ __launch_bounds__(256) void fa_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void fa_fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * C::TILE];  // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];  // [buffer][K tile, V tile]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -74,6 +93,8 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(FwdParams p) {
   const int i16 = lane & 15;
 
   // Largest row blocks first: under a causal mask they carry the most tiles.
+  // Consecutive workgroups go to different XCDs; with B*H a multiple of 8
+  // every workgroup of one head lands on the same XCD and shares its L2.
   const int bh = blockIdx.x % p.BH;
   const int rb = p.n_row_blocks - 1 - blockIdx.x / p.BH;
   const int N = p.N;
@@ -113,38 +134,35 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(FwdParams p) {
       const int id = tid + c * C::THREADS;
       const int r = id / (D / 8);
       const int col = (id % (D / 8)) * 8;
-      const int key = kt * C::BN + r;
-      if (key < N) {
-        kst[c] = *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + col);
-        vst[c] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + col);
-      } else {
-        kst[c] = u32x4{0, 0, 0, 0};
-        vst[c] = u32x4{0, 0, 0, 0};
-      }
+      const int key = min(kt * C::BN + r, N - 1);  // rows past N are masked; any valid row will do
+      kst[c] = *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + col);
+      vst[c] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + col);
     }
   };
   auto store_tile = [&](int buf) {
-    bf16* Ks = smem + buf * 2 * C::TILE;
-    bf16* Vs = Ks + C::TILE;
+    bf16* Ks = smem + buf * C::STAGE;
+    bf16* Vs = Ks + C::KTILE;
 #pragma unroll
     for (int c = 0; c < C::CPT; ++c) {
       const int id = tid + c * C::THREADS;
       const int r = id / (D / 8);
       const int col = (id % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Ks + r * C::STR + col) = kst[c];
-      *reinterpret_cast<u32x4*>(Vs + r * C::STR + col) = vst[c];
+      *reinterpret_cast<u32x4*>(Ks + r * C::STRK + col) = kst[c];
+      *reinterpret_cast<u32x4*>(Vs + r * C::STRV + col) = vst[c];
     }
   };
 
   f32x16 oacc[C::CT];
 #pragma unroll
   for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = f32x16{};
-  float m_run = -INFINITY;  // running max of scaled scores, log2 domain
-  float l_run = 0.f;        // running denominator, this lane half's keys only
+  float m_run = -INFINITY;  // reference max of scaled scores, log2 domain
+  float l_run = 0.f;        // denominator relative to m_run, this lane half's keys only
+  float lb_run = 0.f;       // the same sum over the bf16-rounded probabilities
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
   auto compute = [&](int kt, int buf) {
-    const bf16* Ks = smem + buf * 2 * C::TILE;
-    const bf16* Vs = Ks + C::TILE;
+    const bf16* Ks = smem + buf * C::STAGE;
+    const bf16* Vs = Ks + C::KTILE;
     const int kbase = kt * C::BN;
     // Under the causal mask a wave whose rows all precede this tile sees none of it.
     if (CAUSAL && kbase > wrow0 + 31) return;
@@ -156,7 +174,7 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(FwdParams p) {
     for (int kk = 0; kk < C::KS; ++kk) {
 #pragma unroll
       for (int st = 0; st < C::NT; ++st) {
-        const bf16x8 a = lds_b128(Ks + (32 * st + l32) * C::STR + 16 * kk + 8 * hh);
+        const bf16x8 a = lds_b128(Ks + (32 * st + l32) * C::STRK + 16 * kk + 8 * hh);
         s[st] = mfma32(a, qf[kk], s[st]);
       }
     }
@@ -176,13 +194,20 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int st = 0; st < C::NT; ++st) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[st][v]);
+      for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[st][v], s[st][v + 1]));
     }
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_run, mx * p.sl2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // a row with nothing visible yet
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
+    mx = fmaxf(mx, swap_halves(mx)) * p.sl2;
+    // Move the reference max only if some row of this wave outgrew it by > 2^8.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      lb_run *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < C::CT; ++ct) oacc[ct] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;  // nothing visible yet: all P are 0
 
     bf16x8 pk[2 * C::NT];
     float rs = 0.f;
@@ -197,9 +222,14 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(FwdParams p) {
       pk[2 * st] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       pk[2 * st + 1] = to_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
     }
-    l_run = l_run * alpha + rs;
+    l_run += rs;
 #pragma unroll
-    for (int ct = 0; ct < C::CT; ++ct) oacc[ct] *= alpha;
+    for (int j = 0; j < 2 * C::NT; ++j) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        lb_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pk[j][2 * h], pk[j][2 * h + 1]}, ones,
+                                                 lb_run, false);
+    }
 
     // O^T[c][i] += sum_j V[j][c] P^T[j][i]. MFMA k-slot order within each 16 keys
     // follows the accumulator layout of S^T: lane half hh holds keys 4hh..4hh+3 and
@@ -210,8 +240,8 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int ks = 0; ks < 2 * C::NT; ++ks) {
         const int r0 = 16 * ks + 4 * hh + (i16 >> 2);
-        const i16x4 lo = lds_tr(Vs + r0 * C::STR + n0);
-        const i16x4 hi = lds_tr(Vs + (r0 + 8) * C::STR + n0);
+        const i16x4 lo = lds_tr(Vs + r0 * C::STRV + n0);
+        const i16x4 hi = lds_tr(Vs + (r0 + 8) * C::STRV + n0);
         oacc[ct] = mfma32(cat(lo, hi), pk[ks], oacc[ct]);
       }
     }
@@ -237,7 +267,8 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(FwdParams p) {
 
   // Epilogue: combine the two lane halves' denominators, normalise once.
   const float l_tot = l_run + swap_halves(l_run);
-  const float inv = l_tot > 0.f ? fast_rcp(l_tot) : 0.f;
+  const float lb_tot = lb_run + swap_halves(lb_run);
+  const float inv = lb_tot > 0.f ? fast_rcp(lb_tot) : 0.f;
   if (qrow < N) {
     bf16* orow = p.o + head + (int64_t)qrow * D;
 #pragma unroll
