@@ -183,7 +183,7 @@ def main():
         check(lib.fa_fwd(P(qg), P(kg), P(vg), P(o), P(lse), B, H, N, d, sc, mask, sp))
 
     def pre():
-        check(lib.fa_bwd_preprocess(P(o), P(dog), B, H, N, d, P(ws), wsn, sp))
+        check(lib.fa_bwd_preprocess(P(qg), P(o), P(dog), B, H, N, d, P(ws), wsn, sp))
 
     def main_bwd():
         check(lib.fa_bwd_main(P(qg), P(kg), P(vg), P(dog), P(lse), P(dk), P(dv), B, H, N, d, sc,

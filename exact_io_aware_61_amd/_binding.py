@@ -51,7 +51,7 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp,
                            sz, vp]
-    lib.fa_bwd_preprocess.argtypes = [vp, vp, i32, i32, i32, i32, vp, sz, vp]
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, sz, vp]
     lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz,
                                 vp]
     lib.fa_bwd_finish.argtypes = [vp, i32, i32, i32, i32, f32, vp, sz, vp]
@@ -158,9 +158,9 @@ def backward(q, k, v, o, lse, do, *, causal: bool = False, block_mask=None,
     return dq, dk, dv
 
 
-def bwd_preprocess(o, do, ws):
-    B, H, N, d = _shape(o, do)
-    _check(load().fa_bwd_preprocess(_ptr(o), _ptr(do), B, H, N, d, _ptr(ws), ws.numel(),
+def bwd_preprocess(q, o, do, ws):
+    B, H, N, d = _shape(q, o, do)
+    _check(load().fa_bwd_preprocess(_ptr(q), _ptr(o), _ptr(do), B, H, N, d, _ptr(ws), ws.numel(),
                                     _stream(o)))
 
 

@@ -70,10 +70,23 @@ bool any_overlap(const Range* outs, int n_out, const Range* ins, int n_in) {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace layout: [D_i float32 x BH*N | pad to 256 | dQ accumulator float32 x BH*N*d].
+int padded_rows(int N) {
+  const int r = fa::bwd_row_padding();
+  return (N + r - 1) / r * r;
+}
+
+// Workspace layout, each part starting on a 256-byte boundary:
+//   D_i      float32 [BH * N]
+//   dQ acc   float32 [BH * N * d]
+//   Q^T      bf16    [BH * d * Np]   Np = N rounded up to the row padding
+//   dO^T     bf16    [BH * d * Np]
+size_t ws_part_d(const Shape& s) { return round256((size_t)s.bh() * s.N * sizeof(float)); }
+size_t ws_part_dq(const Shape& s) { return round256((size_t)s.elems() * sizeof(float)); }
+size_t ws_part_t(const Shape& s) {
+  return round256((size_t)s.bh() * s.d * padded_rows(s.N) * 2);
+}
 size_t workspace_bytes(const Shape& s) {
-  return round256((size_t)s.bh() * s.N * sizeof(float)) +
-         round256((size_t)s.elems() * sizeof(float));
+  return ws_part_d(s) + ws_part_dq(s) + 2 * ws_part_t(s);
 }
 
 int check_workspace(const void* ws, size_t bytes, const Shape& s) {
@@ -83,10 +96,15 @@ int check_workspace(const void* ws, size_t bytes, const Shape& s) {
   return FA_OK;
 }
 
-void split_workspace(void* ws, const Shape& s, float** dvec, float** dqacc) {
+void split_workspace(void* ws, const Shape& s, fa::BwdArgs* a) {
   char* base = static_cast<char*>(ws);
-  *dvec = reinterpret_cast<float*>(base);
-  *dqacc = reinterpret_cast<float*>(base + round256((size_t)s.bh() * s.N * sizeof(float)));
+  a->dvec = reinterpret_cast<float*>(base);
+  base += ws_part_d(s);
+  a->dqacc = reinterpret_cast<float*>(base);
+  base += ws_part_dq(s);
+  a->qt = base;
+  a->dot = base + ws_part_t(s);
+  a->Np = padded_rows(s.N);
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
@@ -143,25 +161,26 @@ int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes) {
   return FA_OK;
 }
 
-int fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d,
+int fa_bwd_preprocess(const void* q, const void* o, const void* dout, int B, int H, int N, int d,
                       void* workspace, size_t ws_bytes, void* stream) {
   const Shape s{B, H, N, d};
   FA_TRY(check_shape(s));
   if (s.empty()) return FA_OK;
-  if (!o || !dout) return FA_ERR_NULL;
-  if (!aligned16(o) || !aligned16(dout)) return FA_ERR_ALIGN;
+  if (!q || !o || !dout) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(dout)) return FA_ERR_ALIGN;
   FA_TRY(check_workspace(workspace, ws_bytes, s));
   const int64_t tb = s.elems() * 2;
-  const Range ins[2] = {range(o, tb), range(dout, tb)};
+  const Range ins[3] = {range(q, tb), range(o, tb), range(dout, tb)};
   const Range outs[1] = {range(workspace, (int64_t)workspace_bytes(s))};
-  if (any_overlap(outs, 1, ins, 2)) return FA_ERR_ALIAS;
+  if (any_overlap(outs, 1, ins, 3)) return FA_ERR_ALIAS;
   fa::BwdArgs a{};
+  a.q = q;
   a.o = o;
   a.dout = dout;
   a.BH = (int)s.bh();
   a.N = N;
   a.d = d;
-  split_workspace(workspace, s, &a.dvec, &a.dqacc);
+  split_workspace(workspace, s, &a);
   return launched(fa::launch_bwd_preprocess(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -198,7 +217,7 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, c
   a.d = d;
   a.scale = scale;
   a.mask = m;
-  split_workspace(workspace, s, &a.dvec, &a.dqacc);
+  split_workspace(workspace, s, &a);
   return launched(fa::launch_bwd_main(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -220,7 +239,7 @@ int fa_bwd_finish(void* dq, int B, int H, int N, int d, float scale, void* works
   a.N = N;
   a.d = d;
   a.scale = scale;
-  split_workspace(workspace, s, &a.dvec, &a.dqacc);
+  split_workspace(workspace, s, &a);
   return launched(fa::launch_bwd_finish(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -244,7 +263,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   const Range outs[4] = {range(dq, tb), range(dk, tb), range(dv, tb),
                          range(workspace, (int64_t)workspace_bytes(s))};
   if (any_overlap(outs, 4, ins, 6)) return FA_ERR_ALIAS;
-  FA_TRY(fa_bwd_preprocess(o, dout, B, H, N, d, workspace, ws_bytes, stream));
+  FA_TRY(fa_bwd_preprocess(q, o, dout, B, H, N, d, workspace, ws_bytes, stream));
   FA_TRY(fa_bwd_main(q, k, v, dout, lse, dk, dv, B, H, N, d, scale, mask, workspace, ws_bytes,
                      stream));
   return fa_bwd_finish(dq, B, H, N, d, scale, workspace, ws_bytes, stream);

@@ -8,51 +8,123 @@
 // and merges dQ, the only quantity shared between column blocks, by atomic
 // addition into a float32 accumulator.
 //
-// Per key block (4 waves x 32 keys) and query row block (64 rows), per wave:
-//   S  = Q K_w^T       MFMA, Q rows read from LDS, K_w^T held in VGPRs. The
-//                      accumulator puts one key column in each lane.
-//   P  = 2^(S scale log2e - LSE_i log2e)       (masked pairs -> 0)
-//   dP = dO V_w^T      MFMA, as S
-//   dS = P o (dP - D_i),  D_i = dO_i . O_i (preprocess kernel)
-//   dV_w^T += dO^T P   MFMA, P straight from registers as the B operand,
-//                      dO^T via the transposing LDS read
-//   dK_w^T += Q^T dS   likewise (scale applied once at the end)
-//   dS^T -> LDS; then the workgroup computes dQ_rows = dS K for all 128 keys
-//   (A = dS via transposing reads of dS^T, B = K via transposing reads) and adds
-//   it atomically to the float32 accumulator.
-// The formulas are the chain rule through the softmax; the pages only name it.
+// The gradients are the chain rule through the softmax (the pages only name
+// it): dP = dO V^T, D_i = sum_j P_ij dP_ij = dO_i . O_i, dS = P o (dP - D),
+// dV = P^T dO, dK = scale dS^T Q, dQ = scale dS K.
+//
+// Layout work done once per call (preprocess kernel): D_i, a zeroed float32 dQ
+// accumulator, and transposed copies Q^T and dO^T ([d][rows], rows padded to a
+// multiple of 64). In the transposed copies the rows of every 16-row group are
+// stored in the order 0-3, 8-11, 4-7, 12-15: eight consecutive positions then
+// hold exactly the rows that one half of a wave holds in an MFMA accumulator
+// (rows 4h..4h+3 and 8+4h..8+4h+3), so the dK/dV products read their Q^T/dO^T
+// operand with plain 16-byte LDS reads instead of transposing 8-byte reads.
+//
+// Main kernel, per workgroup of 4 waves = 128 keys; wave w owns keys
+// key0 + 32w .. +31. Per block of BM query rows, per wave:
+//   S  = Q K_w^T, dP = dO V_w^T   MFMA 32x32x16; Q/dO rows from LDS, K_w/V_w in
+//                                 VGPRs. Each lane holds one key column.
+//   P  = 2^(S scale log2e - LSE_i log2e)  (masked pairs -> 0)
+//   dS = P o (dP - D_i)
+//   dV_w^T += dO^T P, dK_w^T += Q^T dS    P, dS straight from registers as the
+//                                 B operand, dO^T/Q^T by 16-byte LDS reads
+//   dS^T -> LDS; then wave w computes one 32x32 tile of dQ = dS K over all 128
+//   keys (dS by transposing LDS reads, its K columns held in VGPRs since the
+//   start) and adds it atomically to the float32 accumulator.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
 namespace fa {
 namespace {
 
+// Position <-> row inside a 16-row group of the transposed copies: positions
+// 4..7 and 8..11 are exchanged (the map is its own inverse).
+__device__ __forceinline__ int perm16(int pos) {
+  const int s = pos & 15;
+  return (pos & ~15) | ((s >= 4 && s < 12) ? (s ^ 12) : s);
+}
+
 // ------------------------------------------------------------------------------------------------
-// Preprocess: D_i = sum_c dO_ic O_ic (float32), and zero the dQ accumulator rows.
+// Preprocess: D_i = sum_c dO_ic O_ic, zero the dQ accumulator, write Q^T and dO^T.
+
+constexpr int kPreRows = 64;  // rows per preprocess workgroup; also the row padding of Q^T/dO^T
+
+struct PreParams {
+  const bf16* q;
+  const bf16* o;
+  const bf16* dout;
+  float* dvec;
+  float* dqacc;
+  bf16* qt;
+  bf16* dot;
+  int BH;
+  int N;
+  int Np;   // padded row count of Q^T / dO^T (multiple of kPreRows)
+};
 
 template <int D>
-__global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const bf16* __restrict__ o,
-                                                         const bf16* __restrict__ dout,
-                                                         float* __restrict__ dvec,
-                                                         float* __restrict__ dqacc,
-                                                         int64_t rows) {
-  constexpr int LPR = D / 8;                 // lanes per row, 8 elements each
-  constexpr int RPB = 256 / LPR;             // rows per block
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int part = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + row * D + 8 * part);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + row * D + 8 * part);
+__global__ __launch_bounds__(256) void fa_bwd_pre_kernel(PreParams p) {
+  constexpr int R = kPreRows;
+  constexpr int STR = D + 8;
+  constexpr int LPR = D / 8;            // 16-byte chunks (lanes) per row
+  constexpr int CH = R * LPR / 256;     // chunks per thread
+  constexpr int TI = D * (R / 8) / 256; // transposed 16-byte outputs per thread per tensor
+  __shared__ __attribute__((aligned(16))) bf16 Qs[R * STR];
+  __shared__ __attribute__((aligned(16))) bf16 Gs[R * STR];
+
+  const int nrb = p.Np / R;
+  const int bh = blockIdx.x / nrb;
+  const int row0 = (blockIdx.x % nrb) * R;
+  const int N = p.N;
+  const int tid = threadIdx.x;
+  const int64_t head = (int64_t)bh * N * D;
+
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
-    f32x4* z = reinterpret_cast<f32x4*>(dqacc + row * D + 8 * part);
-    z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < CH; ++c) {
+    const int id = tid + 256 * c;
+    const int r = id / LPR;
+    const int part = id % LPR;
+    const int row = row0 + r;
+    u32x4 xq = {0, 0, 0, 0}, xg = {0, 0, 0, 0};
+    float acc = 0.f;
+    if (row < N) {
+      const int64_t off = head + (int64_t)row * D + 8 * part;
+      xq = *reinterpret_cast<const u32x4*>(p.q + off);
+      xg = *reinterpret_cast<const u32x4*>(p.dout + off);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(p.o + off);
+      const bf16x8 b = __builtin_bit_cast(bf16x8, xg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+      f32x4* z = reinterpret_cast<f32x4*>(p.dqacc + off);
+      z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // The LPR lanes of one row are consecutive: reduce across them.
+#pragma unroll
+    for (int sh = LPR / 2; sh > 0; sh >>= 1) acc += __shfl_xor(acc, sh);
+    if (row < N && part == 0) p.dvec[(int64_t)bh * N + row] = acc;
+    *reinterpret_cast<u32x4*>(Qs + r * STR + 8 * part) = xq;
+    *reinterpret_cast<u32x4*>(Gs + r * STR + 8 * part) = xg;
   }
+  __syncthreads();
+
+  // Transposed, row-permuted copies: output chunk (column c, positions 8j..8j+7).
 #pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) dvec[row] = acc;
+  for (int t = 0; t < TI; ++t) {
+    const int id = tid + 256 * t;
+    const int col = id / (R / 8);
+    const int j = id % (R / 8);
+    bf16x8 vq, vg;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = perm16(8 * j + e);
+      vq[e] = Qs[r * STR + col];
+      vg[e] = Gs[r * STR + col];
+    }
+    const int64_t off = ((int64_t)bh * D + col) * p.Np + row0 + 8 * j;
+    *reinterpret_cast<bf16x8*>(p.qt + off) = vq;
+    *reinterpret_cast<bf16x8*>(p.dot + off) = vg;
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -77,20 +149,29 @@ template <int D>
 struct BwdCfg {
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int BN = 32 * WAVES;     // keys per workgroup (128)
-  static constexpr int BM = 64;             // query rows per iteration
-  static constexpr int STR = D == 128 ? 152 : 72;  // LDS row stride (elements) for K, Q, dO
-  static constexpr int SSTR = BM + 8;              // LDS row stride of dS^T (72 = 36 dwords)
-  static constexpr int KS = D / 16;
-  static constexpr int CT = D / 32;
-  static constexpr int IT = BM / 32;        // 32-row sub-tiles per row block
-  static constexpr int QCHUNKS = BM * D / 8;
-  static constexpr int QCPT = QCHUNKS / THREADS;
-  static constexpr int KCHUNKS = BN * D / 8;
-  static constexpr int KCPT = KCHUNKS / THREADS;
-  static constexpr int DQT = IT * CT / WAVES;  // dQ output tiles per wave
-  static_assert(QCHUNKS % THREADS == 0 && KCHUNKS % THREADS == 0, "even split");
-  static_assert((IT * CT) % WAVES == 0, "dQ tiles split evenly over waves");
+  static constexpr int BN = 32 * WAVES;           // keys per workgroup (= block-mask granularity)
+  static constexpr int BM = D == 128 ? 32 : 64;   // query rows per iteration
+  static constexpr int IT = BM / 32;              // 32-row sub-tiles
+  static constexpr int RS = BM / 16;              // 16-row MFMA k-steps
+  static constexpr int KS = D / 16;               // 16-column MFMA k-steps over the head dim
+  static constexpr int CT = D / 32;               // 32-column sub-tiles of the head dim
+  static constexpr int QS = BN / 16;              // 16-key MFMA k-steps of dQ = dS K
+  // LDS row strides (bf16 elements), each chosen so that its access pattern is
+  // free of bank conflicts: 16-byte row reads of 32 rows (Q, dO, Q^T, dO^T),
+  // 8-byte writes / transposing reads (dS^T), transposing reads (K, set-up).
+  static constexpr int STRQ = D + 8;              // Q, dO tiles     [BM][STRQ]
+  static constexpr int STRT = BM + 8;             // Q^T, dO^T tiles [D][STRT]
+  static constexpr int STRS = BM + 4;             // dS^T            [BN][STRS]
+  static constexpr int STRK = D + 32;             // K block         [BN][STRK] (set-up only)
+  static constexpr int QTILE = BM * STRQ;
+  static constexpr int TTILE = D * STRT;
+  static constexpr int STAGE = 2 * QTILE + 2 * TTILE;
+  static constexpr int CH = BM * D / 8;           // 16-byte chunks per tile (all four tiles)
+  static constexpr int CPT = CH / THREADS;
+  static_assert(CT * IT == WAVES, "one 32x32 dQ tile per wave");
+  static_assert(CH % THREADS == 0, "tiles split evenly over threads");
+  static_assert(BN * STRK <= 2 * STAGE, "K block fits in the stage buffers");
+  static_assert(kPreRows % BM == 0, "row padding of the transposed copies covers whole row blocks");
 };
 
 struct BwdParams {
@@ -98,6 +179,8 @@ struct BwdParams {
   const bf16* k;
   const bf16* v;
   const bf16* dout;
+  const bf16* qt;
+  const bf16* dot;
   const float* lse;
   const float* dvec;
   float* dqacc;
@@ -105,6 +188,7 @@ struct BwdParams {
   bf16* dv;
   int BH;
   int N;
+  int Np;
   float sl2;    // scale * log2(e)
   float scale;
   const uint8_t* blocks;
@@ -115,12 +199,9 @@ struct BwdParams {
 template <int D, bool CAUSAL, bool BLOCK>
 __global__ __launch_bounds__(256) void fa_bwd_main_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[C::BN * C::STR];
-  __shared__ __attribute__((aligned(16))) bf16 Qs[C::BM * C::STR];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[C::BM * C::STR];
-  __shared__ __attribute__((aligned(16))) bf16 dSt[C::BN * C::SSTR];
-  __shared__ __attribute__((aligned(16))) float Ls[C::BM];   // LSE * log2e (+inf = no row)
-  __shared__ __attribute__((aligned(16))) float Ds[C::BM];
+  __shared__ __attribute__((aligned(16))) bf16 tiles[2 * C::STAGE];  // [stage][Q, dO, Q^T, dO^T]
+  __shared__ __attribute__((aligned(16))) float rowstat[2][2][C::BM]; // [stage][LSE*log2e, D][row]
+  __shared__ __attribute__((aligned(16))) bf16 dSt[C::BN * C::STRS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -138,6 +219,8 @@ __global__ __launch_bounds__(256) void fa_bwd_main_kernel(BwdParams p) {
   const bf16* __restrict__ Kh = p.k + head;
   const bf16* __restrict__ Vh = p.v + head;
   const bf16* __restrict__ dOh = p.dout + head;
+  const bf16* __restrict__ QTh = p.qt + (int64_t)bh * D * p.Np;
+  const bf16* __restrict__ dOTh = p.dot + (int64_t)bh * D * p.Np;
   const float* __restrict__ Lh = p.lse + (int64_t)bh * N;
   const float* __restrict__ Dh = p.dvec + (int64_t)bh * N;
   float* __restrict__ dQh = p.dqacc + head;
@@ -145,26 +228,41 @@ __global__ __launch_bounds__(256) void fa_bwd_main_kernel(BwdParams p) {
   const int key0 = kb * C::BN;
   const int wkey0 = key0 + 32 * wave;
   const int mykey = wkey0 + l32;   // this lane's key column
+  const int itq = wave / C::CT;    // this wave's dQ tile: rows 32*itq.., columns 32*ctq..
+  const int ctq = wave % C::CT;
 
-  // K block -> LDS (for dQ), K_w and V_w operands -> VGPRs.
+  // dQ's B operand: K[16ks + 8hh .. +7][32ctq + l32], through a transposing read
+  // of the K block staged in LDS. Keys past N are clamped (their dS is zero).
+  bf16x8 ktf[C::QS];
+  {
+    bf16* Ks = tiles;
 #pragma unroll
-  for (int c = 0; c < C::KCPT; ++c) {
-    const int id = tid + c * C::THREADS;
-    const int r = id / (D / 8);
-    const int col = (id % (D / 8)) * 8;
-    u32x4 x = {0, 0, 0, 0};
-    if (key0 + r < N) x = *reinterpret_cast<const u32x4*>(Kh + (int64_t)(key0 + r) * D + col);
-    *reinterpret_cast<u32x4*>(Ks + r * C::STR + col) = x;
+    for (int c = 0; c < C::BN * D / 8 / C::THREADS; ++c) {
+      const int id = tid + c * C::THREADS;
+      const int r = id / (D / 8);
+      const int col = (id % (D / 8)) * 8;
+      const int key = min(key0 + r, N - 1);
+      *reinterpret_cast<u32x4*>(Ks + r * C::STRK + col) =
+          *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + col);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < C::QS; ++ks) {
+      const int r0 = 16 * ks + 8 * hh + (i16 >> 2);
+      const int c0 = 32 * ctq + 16 * (g16 & 1) + 4 * (i16 & 3);
+      ktf[ks] = cat(lds_tr(Ks + r0 * C::STRK + c0), lds_tr(Ks + (r0 + 4) * C::STRK + c0));
+    }
+    __syncthreads();  // the staging area becomes the row-block buffers
   }
+
+  // S / dP B operands: K and V rows of this lane's key, k = head-dim chunks.
   bf16x8 kf[C::KS], vf[C::KS];
+  {
+    const int key = min(mykey, N - 1);
 #pragma unroll
-  for (int kk = 0; kk < C::KS; ++kk) {
-    if (mykey < N) {
-      kf[kk] = *reinterpret_cast<const bf16x8*>(Kh + (int64_t)mykey * D + 16 * kk + 8 * hh);
-      vf[kk] = *reinterpret_cast<const bf16x8*>(Vh + (int64_t)mykey * D + 16 * kk + 8 * hh);
-    } else {
-      kf[kk] = bf16x8{};
-      vf[kk] = bf16x8{};
+    for (int kk = 0; kk < C::KS; ++kk) {
+      kf[kk] = *reinterpret_cast<const bf16x8*>(Kh + (int64_t)key * D + 16 * kk + 8 * hh);
+      vf[kk] = *reinterpret_cast<const bf16x8*>(Vh + (int64_t)key * D + 16 * kk + 8 * hh);
     }
   }
 
@@ -175,46 +273,82 @@ __global__ __launch_bounds__(256) void fa_bwd_main_kernel(BwdParams p) {
     dv[ct] = f32x16{};
   }
 
-  // Row-block range: under causal, rows before key0 see none of these keys.
+  // Row blocks: under causal, rows before key0 see none of these keys.
   const int n_rb = (N + C::BM - 1) / C::BM;
   const int rb_begin = CAUSAL ? key0 / C::BM : 0;
   auto kept = [&](int rb) -> bool {
     if (!BLOCK) return true;
     return p.blocks[bh * p.blocks_bh_stride + (int64_t)((rb * C::BM) / 128) * p.nb + kb] != 0;
   };
+  auto next_kept = [&](int rb) -> int {
+    ++rb;
+    while (rb < n_rb && !kept(rb)) ++rb;
+    return rb;
+  };
 
-  for (int rb = rb_begin; rb < n_rb; ++rb) {
-    if (!kept(rb)) continue;
+  u32x4 sq[C::CPT], sdo[C::CPT], sqt[C::CPT], sdot[C::CPT];
+  float s_l = 0.f, s_d = 0.f;
+  int row_next = 0;   // first row of the staged block
+  auto load_rb = [&](int rb) {
     const int row0 = rb * C::BM;
-    // Q, dO row block -> LDS; LSE (log2 domain) and D -> LDS.
+    row_next = row0;
 #pragma unroll
-    for (int c = 0; c < C::QCPT; ++c) {
+    for (int c = 0; c < C::CPT; ++c) {
       const int id = tid + c * C::THREADS;
       const int r = id / (D / 8);
       const int col = (id % (D / 8)) * 8;
-      u32x4 xq = {0, 0, 0, 0}, xo = {0, 0, 0, 0};
-      if (row0 + r < N) {
-        xq = *reinterpret_cast<const u32x4*>(Qh + (int64_t)(row0 + r) * D + col);
-        xo = *reinterpret_cast<const u32x4*>(dOh + (int64_t)(row0 + r) * D + col);
-      }
-      *reinterpret_cast<u32x4*>(Qs + r * C::STR + col) = xq;
-      *reinterpret_cast<u32x4*>(dOs + r * C::STR + col) = xo;
+      const int64_t off = (int64_t)min(row0 + r, N - 1) * D + col;  // rows past N get P = 0
+      sq[c] = *reinterpret_cast<const u32x4*>(Qh + off);
+      sdo[c] = *reinterpret_cast<const u32x4*>(dOh + off);
+      const int dd = id / (C::BM / 8);
+      const int j = id % (C::BM / 8);
+      const int64_t toff = (int64_t)dd * p.Np + row0 + 8 * j;
+      sqt[c] = *reinterpret_cast<const u32x4*>(QTh + toff);
+      sdot[c] = *reinterpret_cast<const u32x4*>(dOTh + toff);
+    }
+    // Raw values only: they are first used after the compute phase, so the
+    // loads stay in flight across it (using them here would wait for every
+    // load issued above).
+    if (tid < C::BM) {
+      const int row = min(row0 + tid, N - 1);
+      s_l = Lh[row];
+      s_d = Dh[row];
+    }
+  };
+  auto store_rb = [&](int buf) {
+    bf16* Qs = tiles + buf * C::STAGE;
+    bf16* dOs = Qs + C::QTILE;
+    bf16* QTs = dOs + C::QTILE;
+    bf16* dOTs = QTs + C::TTILE;
+#pragma unroll
+    for (int c = 0; c < C::CPT; ++c) {
+      const int id = tid + c * C::THREADS;
+      const int r = id / (D / 8);
+      const int col = (id % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(Qs + r * C::STRQ + col) = sq[c];
+      *reinterpret_cast<u32x4*>(dOs + r * C::STRQ + col) = sdo[c];
+      const int dd = id / (C::BM / 8);
+      const int j = id % (C::BM / 8);
+      *reinterpret_cast<u32x4*>(QTs + dd * C::STRT + 8 * j) = sqt[c];
+      *reinterpret_cast<u32x4*>(dOTs + dd * C::STRT + 8 * j) = sdot[c];
     }
     if (tid < C::BM) {
-      const int row = row0 + tid;
-      float l2 = INFINITY, dd = 0.f;
-      if (row < N) {
-        const float lse = Lh[row];
-        // A row with no visible key has LSE = -inf and contributes nothing.
-        l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
-        dd = Dh[row];
-      }
-      Ls[tid] = l2;
-      Ds[tid] = dd;
+      // +inf: the row contributes nothing (past N, or no visible key at all).
+      const bool live = row_next + tid < N && s_l != -INFINITY;
+      rowstat[buf][0][tid] = live ? s_l * kLog2e : INFINITY;
+      rowstat[buf][1][tid] = live ? s_d : 0.f;
     }
-    __syncthreads();
+  };
 
-    // S and dP for this wave's 32 keys and the 64 rows (two 32-row sub-tiles).
+  auto compute = [&](int rb, int buf) {
+    const bf16* Qs = tiles + buf * C::STAGE;
+    const bf16* dOs = Qs + C::QTILE;
+    const bf16* QTs = dOs + C::QTILE;
+    const bf16* dOTs = QTs + C::TTILE;
+    const float* Ls = rowstat[buf][0];
+    const float* Ds = rowstat[buf][1];
+    const int row0 = rb * C::BM;
+
     f32x16 s[C::IT], dp[C::IT];
 #pragma unroll
     for (int it = 0; it < C::IT; ++it) {
@@ -225,15 +359,15 @@ __global__ __launch_bounds__(256) void fa_bwd_main_kernel(BwdParams p) {
     for (int kk = 0; kk < C::KS; ++kk) {
 #pragma unroll
       for (int it = 0; it < C::IT; ++it) {
-        const bf16x8 a = lds_b128(Qs + (32 * it + l32) * C::STR + 16 * kk + 8 * hh);
+        const bf16x8 a = lds_b128(Qs + (32 * it + l32) * C::STRQ + 16 * kk + 8 * hh);
         s[it] = mfma32(a, kf[kk], s[it]);
-        const bf16x8 b = lds_b128(dOs + (32 * it + l32) * C::STR + 16 * kk + 8 * hh);
+        const bf16x8 b = lds_b128(dOs + (32 * it + l32) * C::STRQ + 16 * kk + 8 * hh);
         dp[it] = mfma32(b, vf[kk], dp[it]);
       }
     }
     // s[it][v]: row row0 + 32*it + 8*(v/4) + 4*hh + v%4, key mykey.
     const bool edge = (CAUSAL && row0 < wkey0 + 31) || (key0 + C::BN > N);
-    bf16x8 pk[2 * C::IT], dsk[2 * C::IT];
+    bf16x8 pk[C::RS], dsk[C::RS];
 #pragma unroll
     for (int it = 0; it < C::IT; ++it) {
       float pv[16], dsv[16];
@@ -262,52 +396,59 @@ __global__ __launch_bounds__(256) void fa_bwd_main_kernel(BwdParams p) {
       // dS^T row (key) of this lane, four consecutive query rows per store.
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        *reinterpret_cast<bf16x4*>(dSt + (32 * wave + l32) * C::SSTR + 32 * it + 8 * g + 4 * hh) =
+        *reinterpret_cast<bf16x4*>(dSt + (32 * wave + l32) * C::STRS + 32 * it + 8 * g + 4 * hh) =
             to_bf16x4(dsv[4 * g], dsv[4 * g + 1], dsv[4 * g + 2], dsv[4 * g + 3]);
       }
     }
 
-    // dV^T += dO^T P and dK^T += Q^T dS. MFMA k-slots (query rows) follow the
-    // accumulator layout: lane half hh holds rows 4hh..4hh+3 and 8+4hh..8+4hh+3 of
-    // each 16, so the transposed operand is read as those two groups of four rows.
+    // dV^T += dO^T P and dK^T += Q^T dS; the permuted row order of the transposed
+    // tiles makes positions 16ks + 8hh .. +7 the rows this lane half holds in P, dS.
 #pragma unroll
     for (int ct = 0; ct < C::CT; ++ct) {
-      const int n0 = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
 #pragma unroll
-      for (int ks = 0; ks < 2 * C::IT; ++ks) {
-        const int r0 = 16 * ks + 4 * hh + (i16 >> 2);
-        const bf16x8 ot = cat(lds_tr(dOs + r0 * C::STR + n0), lds_tr(dOs + (r0 + 8) * C::STR + n0));
+      for (int ks = 0; ks < C::RS; ++ks) {
+        const bf16x8 ot = lds_b128(dOTs + (32 * ct + l32) * C::STRT + 16 * ks + 8 * hh);
         dv[ct] = mfma32(ot, pk[ks], dv[ct]);
-        const bf16x8 qt = cat(lds_tr(Qs + r0 * C::STR + n0), lds_tr(Qs + (r0 + 8) * C::STR + n0));
+        const bf16x8 qt = lds_b128(QTs + (32 * ct + l32) * C::STRT + 16 * ks + 8 * hh);
         dk[ct] = mfma32(qt, dsk[ks], dk[ct]);
       }
     }
-    __syncthreads();   // dS^T complete; Q/dO no longer read in this iteration
+    __syncthreads();   // dS^T complete
 
-    // dQ[rows][c] += sum over the 128 keys of dS[row][key] K[key][c].
+    // dQ[rows 32itq..][cols 32ctq..] += sum over the 128 keys of dS[row][key] K[key][col].
+    f32x16 acc = f32x16{};
 #pragma unroll
-    for (int t = 0; t < C::DQT; ++t) {
-      const int tile = wave + C::WAVES * t;
-      const int it = tile % C::IT;
-      const int ct = tile / C::IT;
-      f32x16 acc = f32x16{};
-      const int na = 32 * it + 16 * (g16 & 1) + 4 * (i16 & 3);
-      const int nb = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
-#pragma unroll
-      for (int ks = 0; ks < C::BN / 16; ++ks) {
-        const int r0 = 16 * ks + 4 * hh + (i16 >> 2);
-        const bf16x8 a = cat(lds_tr(dSt + r0 * C::SSTR + na), lds_tr(dSt + (r0 + 8) * C::SSTR + na));
-        const bf16x8 b = cat(lds_tr(Ks + r0 * C::STR + nb), lds_tr(Ks + (r0 + 8) * C::STR + nb));
-        acc = mfma32(a, b, acc);
-      }
-      // acc[v]: row row0 + 32*it + 8*(v/4) + 4*hh + v%4, column 32*ct + l32.
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = row0 + 32 * it + 8 * (v / 4) + 4 * hh + (v % 4);
-        if (row < N) unsafeAtomicAdd(dQh + (int64_t)row * D + 32 * ct + l32, acc[v]);
-      }
+    for (int ks = 0; ks < C::QS; ++ks) {
+      const int r0 = 16 * ks + 8 * hh + (i16 >> 2);
+      const int c0 = 32 * itq + 16 * (g16 & 1) + 4 * (i16 & 3);
+      const bf16x8 a = cat(lds_tr(dSt + r0 * C::STRS + c0), lds_tr(dSt + (r0 + 4) * C::STRS + c0));
+      acc = mfma32(a, ktf[ks], acc);
     }
-    __syncthreads();   // all dS^T / Q / dO reads done before the next row block overwrites them
+    // acc[v]: row row0 + 32*itq + 8*(v/4) + 4*hh + v%4, column 32*ctq + l32. Rows
+    // past N have dS = 0, so their (exactly zero) sums go to row N-1 unchanged.
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = min(row0 + 32 * itq + 8 * (v / 4) + 4 * hh + (v % 4), N - 1);
+      unsafeAtomicAdd(dQh + (int64_t)row * D + 32 * ctq + l32, acc[v]);
+    }
+  };
+
+  int rb = rb_begin;
+  if (rb < n_rb && !kept(rb)) rb = next_kept(rb);
+  if (rb < n_rb) {
+    load_rb(rb);
+    store_rb(0);
+    __syncthreads();
+    int buf = 0;
+    while (rb < n_rb) {
+      const int rn = next_kept(rb);
+      if (rn < n_rb) load_rb(rn);
+      compute(rb, buf);
+      if (rn < n_rb) store_rb(buf ^ 1);
+      __syncthreads();   // next block staged; dS^T and this block's buffers free
+      buf ^= 1;
+      rb = rn;
+    }
   }
 
   // dK^T / dV^T accumulators: lane holds key mykey, columns 32*ct + 8*g + 4*hh + r.
@@ -337,6 +478,8 @@ hipError_t launch_main_d(const BwdArgs& a, hipStream_t stream) {
   p.k = static_cast<const bf16*>(a.k);
   p.v = static_cast<const bf16*>(a.v);
   p.dout = static_cast<const bf16*>(a.dout);
+  p.qt = static_cast<const bf16*>(a.qt);
+  p.dot = static_cast<const bf16*>(a.dot);
   p.lse = a.lse;
   p.dvec = a.dvec;
   p.dqacc = a.dqacc;
@@ -344,6 +487,7 @@ hipError_t launch_main_d(const BwdArgs& a, hipStream_t stream) {
   p.dv = static_cast<bf16*>(a.dv);
   p.BH = a.BH;
   p.N = a.N;
+  p.Np = a.Np;
   p.sl2 = a.scale * kLog2e;
   p.scale = a.scale;
   p.blocks = a.mask.blocks;
@@ -369,19 +513,25 @@ hipError_t launch_main_d(const BwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+int bwd_row_padding() { return kPreRows; }
+
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.BH * a.N;
-  const int lpr = a.d / 8;
-  const int rpb = 256 / lpr;
-  const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-  const bf16* o = static_cast<const bf16*>(a.o);
-  const bf16* dout = static_cast<const bf16*>(a.dout);
+  PreParams p;
+  p.q = static_cast<const bf16*>(a.q);
+  p.o = static_cast<const bf16*>(a.o);
+  p.dout = static_cast<const bf16*>(a.dout);
+  p.dvec = a.dvec;
+  p.dqacc = a.dqacc;
+  p.qt = static_cast<bf16*>(a.qt);
+  p.dot = static_cast<bf16*>(a.dot);
+  p.BH = a.BH;
+  p.N = a.N;
+  p.Np = a.Np;
+  const dim3 grid((unsigned)(a.BH * (a.Np / kPreRows)));
   if (a.d == 128)
-    hipLaunchKernelGGL((fa_bwd_pre_kernel<128>), grid, dim3(256), 0, stream, o, dout, a.dvec,
-                       a.dqacc, rows);
+    hipLaunchKernelGGL((fa_bwd_pre_kernel<128>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((fa_bwd_pre_kernel<64>), grid, dim3(256), 0, stream, o, dout, a.dvec,
-                       a.dqacc, rows);
+    hipLaunchKernelGGL((fa_bwd_pre_kernel<64>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

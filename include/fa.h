@@ -93,9 +93,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, const fa_mask_t* mask, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: the row terms D_i = dO_i . O_i
- * ([B, H, N] float32) and the float32 dQ accumulator ([B, H, N, d]), each
- * 256-byte aligned. Writes the size to *bytes. Pure host arithmetic.
+ * Bytes of device workspace fa_bwd needs, written to *bytes (pure host
+ * arithmetic). The workspace holds, each part 256-byte aligned: the row terms
+ * D_i = dO_i . O_i ([B, H, N] float32), the float32 dQ accumulator
+ * ([B, H, N, d]), and transposed bf16 copies of Q and dO ([B, H, d, Np] each,
+ * Np = N rounded up to a multiple of 64).
  */
 int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);
 
@@ -119,15 +121,17 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 
 /*
  * The three stages of fa_bwd, exposed so a caller can time or schedule them
- * separately; calling them in order on one stream equals fa_bwd.
- *   fa_bwd_preprocess : D_i = sum_c dO_ic O_ic into the workspace, and zeroes
- *                       the float32 dQ accumulator.
+ * separately; calling them in order on one stream, with one workspace, equals
+ * fa_bwd.
+ *   fa_bwd_preprocess : D_i = sum_c dO_ic O_ic into the workspace, zeroes the
+ *                       float32 dQ accumulator, and writes the transposed
+ *                       copies of Q and dO.
  *   fa_bwd_main       : dK, dV (written as bf16) and dQ accumulated in float32
  *                       in the workspace.
  *   fa_bwd_finish     : writes dq = bf16(scale * dQ accumulator).
  * Argument meanings and checks are those of fa_bwd.
  */
-int fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d,
+int fa_bwd_preprocess(const void* q, const void* o, const void* dout, int B, int H, int N, int d,
                       void* workspace, size_t workspace_bytes, void* stream);
 int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
                 const float* lse, void* dk, void* dv,

@@ -56,7 +56,9 @@ def test_workspace_size_arithmetic(lib):
     for B, H, N, d in [(2, 16, 8192, 128), (1, 1, 1, 64), (4, 16, 16384, 64), (3, 5, 1000, 128)]:
         assert lib.fa_bwd_workspace_size(B, H, N, d, ctypes.byref(n)) == OK
         r256 = lambda x: (x + 255) // 256 * 256
-        assert n.value == r256(B * H * N * 4) + r256(B * H * N * d * 4)
+        Np = (N + 63) // 64 * 64
+        assert n.value == (r256(B * H * N * 4) + r256(B * H * N * d * 4)
+                           + 2 * r256(B * H * d * Np * 2))
     assert lib.fa_bwd_workspace_size(1, 1, 1, 96, ctypes.byref(n)) == SHAPE
     assert lib.fa_bwd_workspace_size(-1, 1, 1, 64, ctypes.byref(n)) == SHAPE
     assert lib.fa_bwd_workspace_size(1, 1, 1, 64, None) == NULL
@@ -119,7 +121,8 @@ def test_bwd_rejects_bad_arguments(lib):
     assert bwd(ws_bytes=need - 1) == WS
     assert bwd(ws_ptr=ctypes.c_void_p(0x90004)) == ALIGN
     assert bwd(dq=ctypes.c_void_p(0x10000 + 64)) == ALIAS   # dq overlaps q
-    assert lib.fa_bwd_preprocess(None, P[1], 1, 2, 256, 64, ws, need, STREAM) == NULL
+    assert lib.fa_bwd_preprocess(None, P[1], P[2], 1, 2, 256, 64, ws, need, STREAM) == NULL
+    assert lib.fa_bwd_preprocess(P[0], P[1], P[2], 1, 2, 256, 64, ws, need - 1, STREAM) == WS
     assert lib.fa_bwd_main(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 2, 256, 64, 0.125, None,
                            ws, 16, STREAM) == WS
     assert lib.fa_bwd_finish(P[5], 1, 2, 256, 64, 0.125, None, need, STREAM) == WS
