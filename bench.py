@@ -1,8 +1,8 @@
 """Benchmark: exact attention forward + backward through the HIP library (libfa.so).
 
 One step = one pass of the whole path on one batch of synthetic input:
-fa_fwd, then the backward's three stages (fa_bwd_preprocess, fa_bwd_main,
-fa_bwd_finish, which together are fa_bwd). Inputs, outputs and workspace are
+fa_fwd, then the backward's three stages (fa_bwd_preprocess, fa_bwd_dkdv,
+fa_bwd_dq, which together are fa_bwd). Inputs, outputs and workspace are
 resident in device memory before the timed region starts.
 
     python bench.py [--steps K] [--warmup W] [--workload causal8k] [--cpu-seconds 10]
@@ -185,15 +185,16 @@ def main():
     def pre():
         check(lib.fa_bwd_preprocess(P(qg), P(o), P(dog), B, H, N, d, P(ws), wsn, sp))
 
-    def main_bwd():
-        check(lib.fa_bwd_main(P(qg), P(kg), P(vg), P(dog), P(lse), P(dk), P(dv), B, H, N, d, sc,
+    def dkdv():
+        check(lib.fa_bwd_dkdv(P(qg), P(kg), P(vg), P(dog), P(lse), P(dk), P(dv), B, H, N, d, sc,
                               mask, P(ws), wsn, sp))
 
-    def fin():
-        check(lib.fa_bwd_finish(P(dq), B, H, N, d, sc, P(ws), wsn, sp))
+    def dqk():
+        check(lib.fa_bwd_dq(P(qg), P(kg), P(vg), P(dog), P(lse), P(dq), B, H, N, d, sc, mask,
+                            P(ws), wsn, sp))
 
     stages = [("fa_fwd_kernel", fwd), ("fa_bwd_pre_kernel", pre),
-              ("fa_bwd_main_kernel", main_bwd), ("fa_bwd_finish_kernel", fin)]
+              ("fa_bwd_dkdv_kernel", dkdv), ("fa_bwd_dq_kernel", dqk)]
 
     for i in range(args.warmup):
         for _, f in stages:
@@ -224,7 +225,11 @@ def main():
     ms_per_step = wall / K * 1e3
     value = step_flop / (ms_per_step * 1e-3) / 1e12
 
-    kernel_flop = {"fa_fwd_kernel": fwd_flop, "fa_bwd_main_kernel": 2.5 * fwd_flop}
+    # Algorithmic FLOPs per kernel: the dK/dV kernel's four products (S, dP, dV,
+    # dK) and the dQ kernel's dQ product count; the dQ kernel's recompute of S
+    # and dP is not counted, so the two sum to the backward's five products.
+    kernel_flop = {"fa_fwd_kernel": fwd_flop, "fa_bwd_dkdv_kernel": 2.0 * fwd_flop,
+                   "fa_bwd_dq_kernel": 0.5 * fwd_flop}
     dom = max(kernel_flop, key=lambda n: per[n])
     achieved = kernel_flop[dom] / (per[dom] * 1e-3) / 1e12
     digest = source_digest()

@@ -13,9 +13,9 @@ device memory. This package is the thin Python binding:
 Build the library first: python -m exact_io_aware_61_amd.build
 """
 from ._binding import (EXPORTS, FA_MASK_BLOCK, FA_MASK_CAUSAL, LIB_PATH, MASK_BLOCK_SIZE, FaError,
-                       attention, backward, bwd_finish, bwd_main, bwd_preprocess,
+                       attention, backward, bwd_dkdv, bwd_dq, bwd_preprocess,
                        bwd_workspace_size, default_scale, forward, load, strerror, workspace)
 
 __all__ = ["EXPORTS", "FA_MASK_BLOCK", "FA_MASK_CAUSAL", "LIB_PATH", "MASK_BLOCK_SIZE", "FaError",
-           "attention", "backward", "bwd_finish", "bwd_main", "bwd_preprocess",
+           "attention", "backward", "bwd_dkdv", "bwd_dq", "bwd_preprocess",
            "bwd_workspace_size", "default_scale", "forward", "load", "strerror", "workspace"]

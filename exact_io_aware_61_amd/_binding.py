@@ -19,8 +19,8 @@ FA_MASK_CAUSAL = 1
 FA_MASK_BLOCK = 2
 MASK_BLOCK_SIZE = 128
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess", "fa_bwd_main",
-           "fa_bwd_finish", "fa_strerror")
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess", "fa_bwd_dkdv",
+           "fa_bwd_dq", "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -52,9 +52,9 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp,
                            sz, vp]
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, sz, vp]
-    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz,
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz,
                                 vp]
-    lib.fa_bwd_finish.argtypes = [vp, i32, i32, i32, i32, f32, vp, sz, vp]
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz, vp]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.fa_strerror.argtypes = [ctypes.c_int]
@@ -164,19 +164,22 @@ def bwd_preprocess(q, o, do, ws):
                                     _stream(o)))
 
 
-def bwd_main(q, k, v, do, lse, dk, dv, ws, *, causal=False, block_mask=None, scale=None):
+def bwd_dkdv(q, k, v, do, lse, dk, dv, ws, *, causal=False, block_mask=None, scale=None):
     B, H, N, d = _shape(q, k, v, do)
     scale = default_scale(d) if scale is None else float(scale)
     mptr, keep = _mask(causal, block_mask, B, H, N, q.device)
-    _check(load().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv),
+    _check(load().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv),
                               B, H, N, d, scale, mptr, _ptr(ws), ws.numel(), _stream(q)))
     del keep
 
 
-def bwd_finish(dq, ws, *, scale=None):
-    B, H, N, d = (int(x) for x in dq.shape)
+def bwd_dq(q, k, v, do, lse, dq, ws, *, causal=False, block_mask=None, scale=None):
+    B, H, N, d = _shape(q, k, v, do)
     scale = default_scale(d) if scale is None else float(scale)
-    _check(load().fa_bwd_finish(_ptr(dq), B, H, N, d, scale, _ptr(ws), ws.numel(), _stream(dq)))
+    mptr, keep = _mask(causal, block_mask, B, H, N, q.device)
+    _check(load().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dq),
+                            B, H, N, d, scale, mptr, _ptr(ws), ws.numel(), _stream(q)))
+    del keep
 
 
 class _AttentionFn(torch.autograd.Function):

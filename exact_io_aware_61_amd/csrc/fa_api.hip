@@ -77,17 +77,13 @@ int padded_rows(int N) {
 
 // Workspace layout, each part starting on a 256-byte boundary:
 //   D_i      float32 [BH * N]
-//   dQ acc   float32 [BH * N * d]
 //   Q^T      bf16    [BH * d * Np]   Np = N rounded up to the row padding
 //   dO^T     bf16    [BH * d * Np]
 size_t ws_part_d(const Shape& s) { return round256((size_t)s.bh() * s.N * sizeof(float)); }
-size_t ws_part_dq(const Shape& s) { return round256((size_t)s.elems() * sizeof(float)); }
 size_t ws_part_t(const Shape& s) {
   return round256((size_t)s.bh() * s.d * padded_rows(s.N) * 2);
 }
-size_t workspace_bytes(const Shape& s) {
-  return ws_part_d(s) + ws_part_dq(s) + 2 * ws_part_t(s);
-}
+size_t workspace_bytes(const Shape& s) { return ws_part_d(s) + 2 * ws_part_t(s); }
 
 int check_workspace(const void* ws, size_t bytes, const Shape& s) {
   if (ws == nullptr) return FA_ERR_WORKSPACE;
@@ -100,8 +96,6 @@ void split_workspace(void* ws, const Shape& s, fa::BwdArgs* a) {
   char* base = static_cast<char*>(ws);
   a->dvec = reinterpret_cast<float*>(base);
   base += ws_part_d(s);
-  a->dqacc = reinterpret_cast<float*>(base);
-  base += ws_part_dq(s);
   a->qt = base;
   a->dot = base + ws_part_t(s);
   a->Np = padded_rows(s.N);
@@ -114,6 +108,49 @@ int launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
     const int rc_ = (expr);   \
     if (rc_ != FA_OK) return rc_; \
   } while (0)
+
+// Checks shared by the two gradient stages (dK/dV and dQ); outs are the stage's
+// bf16 outputs (n_out of them). On success fills *a; *empty reports a zero extent.
+int check_grad_stage(const void* q, const void* k, const void* v, const void* dout,
+                     const float* lse, void* const* outs, int n_out, int B, int H, int N, int d,
+                     float scale, const fa_mask_t* mask, void* workspace, size_t ws_bytes,
+                     fa::BwdArgs* a, bool* empty) {
+  const Shape s{B, H, N, d};
+  FA_TRY(check_shape(s));
+  FA_TRY(check_scale(scale));
+  fa::MaskArgs m;
+  FA_TRY(check_mask(mask, s, &m));
+  *empty = s.empty();
+  if (*empty) return FA_OK;
+  if (!q || !k || !v || !dout || !lse) return FA_ERR_NULL;
+  for (int i = 0; i < n_out; ++i)
+    if (!outs[i]) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned4(lse))
+    return FA_ERR_ALIGN;
+  for (int i = 0; i < n_out; ++i)
+    if (!aligned16(outs[i])) return FA_ERR_ALIGN;
+  FA_TRY(check_workspace(workspace, ws_bytes, s));
+  const int64_t tb = s.elems() * 2;
+  const Range ins[6] = {range(q, tb), range(k, tb), range(v, tb), range(dout, tb),
+                        range(lse, s.bh() * N * 4),
+                        range(workspace, (int64_t)workspace_bytes(s))};
+  Range out_r[2];
+  for (int i = 0; i < n_out; ++i) out_r[i] = range(outs[i], tb);
+  if (any_overlap(out_r, n_out, ins, 6)) return FA_ERR_ALIAS;
+  *a = fa::BwdArgs{};
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->dout = dout;
+  a->lse = lse;
+  a->BH = (int)s.bh();
+  a->N = N;
+  a->d = d;
+  a->scale = scale;
+  a->mask = m;
+  split_workspace(workspace, s, a);
+  return FA_OK;
+}
 
 }  // namespace
 
@@ -184,63 +221,31 @@ int fa_bwd_preprocess(const void* q, const void* o, const void* dout, int B, int
   return launched(fa::launch_bwd_preprocess(a, static_cast<hipStream_t>(stream)));
 }
 
-int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                 void* dk, void* dv, int B, int H, int N, int d, float scale,
                 const fa_mask_t* mask, void* workspace, size_t ws_bytes, void* stream) {
-  const Shape s{B, H, N, d};
-  FA_TRY(check_shape(s));
-  FA_TRY(check_scale(scale));
-  fa::MaskArgs m;
-  FA_TRY(check_mask(mask, s, &m));
-  if (s.empty()) return FA_OK;
-  if (!q || !k || !v || !dout || !lse || !dk || !dv) return FA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned4(lse) ||
-      !aligned16(dk) || !aligned16(dv))
-    return FA_ERR_ALIGN;
-  FA_TRY(check_workspace(workspace, ws_bytes, s));
-  const int64_t tb = s.elems() * 2;
-  const Range ins[5] = {range(q, tb), range(k, tb), range(v, tb), range(dout, tb),
-                        range(lse, s.bh() * N * 4)};
-  const Range outs[3] = {range(dk, tb), range(dv, tb),
-                         range(workspace, (int64_t)workspace_bytes(s))};
-  if (any_overlap(outs, 3, ins, 5)) return FA_ERR_ALIAS;
-  fa::BwdArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.dout = dout;
-  a.lse = lse;
+  void* const outs[2] = {dk, dv};
+  fa::BwdArgs a;
+  bool empty = false;
+  FA_TRY(check_grad_stage(q, k, v, dout, lse, outs, 2, B, H, N, d, scale, mask, workspace,
+                          ws_bytes, &a, &empty));
+  if (empty) return FA_OK;
   a.dk = dk;
   a.dv = dv;
-  a.BH = (int)s.bh();
-  a.N = N;
-  a.d = d;
-  a.scale = scale;
-  a.mask = m;
-  split_workspace(workspace, s, &a);
-  return launched(fa::launch_bwd_main(a, static_cast<hipStream_t>(stream)));
+  return launched(fa::launch_bwd_dkdv(a, static_cast<hipStream_t>(stream)));
 }
 
-int fa_bwd_finish(void* dq, int B, int H, int N, int d, float scale, void* workspace,
-                  size_t ws_bytes, void* stream) {
-  const Shape s{B, H, N, d};
-  FA_TRY(check_shape(s));
-  FA_TRY(check_scale(scale));
-  if (s.empty()) return FA_OK;
-  if (!dq) return FA_ERR_NULL;
-  if (!aligned16(dq)) return FA_ERR_ALIGN;
-  FA_TRY(check_workspace(workspace, ws_bytes, s));
-  const Range ins[1] = {range(workspace, (int64_t)workspace_bytes(s))};
-  const Range outs[1] = {range(dq, s.elems() * 2)};
-  if (any_overlap(outs, 1, ins, 1)) return FA_ERR_ALIAS;
-  fa::BwdArgs a{};
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+              void* dq, int B, int H, int N, int d, float scale, const fa_mask_t* mask,
+              void* workspace, size_t ws_bytes, void* stream) {
+  void* const outs[1] = {dq};
+  fa::BwdArgs a;
+  bool empty = false;
+  FA_TRY(check_grad_stage(q, k, v, dout, lse, outs, 1, B, H, N, d, scale, mask, workspace,
+                          ws_bytes, &a, &empty));
+  if (empty) return FA_OK;
   a.dq = dq;
-  a.BH = (int)s.bh();
-  a.N = N;
-  a.d = d;
-  a.scale = scale;
-  split_workspace(workspace, s, &a);
-  return launched(fa::launch_bwd_finish(a, static_cast<hipStream_t>(stream)));
+  return launched(fa::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -264,9 +269,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                          range(workspace, (int64_t)workspace_bytes(s))};
   if (any_overlap(outs, 4, ins, 6)) return FA_ERR_ALIAS;
   FA_TRY(fa_bwd_preprocess(q, o, dout, B, H, N, d, workspace, ws_bytes, stream));
-  FA_TRY(fa_bwd_main(q, k, v, dout, lse, dk, dv, B, H, N, d, scale, mask, workspace, ws_bytes,
+  FA_TRY(fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, H, N, d, scale, mask, workspace, ws_bytes,
                      stream));
-  return fa_bwd_finish(dq, B, H, N, d, scale, workspace, ws_bytes, stream);
+  return fa_bwd_dq(q, k, v, dout, lse, dq, B, H, N, d, scale, mask, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

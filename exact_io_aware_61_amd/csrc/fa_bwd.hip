@@ -1,26 +1,26 @@
-// Backward attention for gfx950: dQ, dK, dV with P recomputed from the saved LSE.
+// Backward attention for gfx950, dK/dV part, with P recomputed from the saved LSE.
 //
 // Recomputation (lecture summary on FlashAttention v1, part 4.2): no N x N matrix
 // is read back; each tile of S and P is rebuilt on chip from Q, K and the row
 // logsumexp, the only statistic kept (FlashAttention-2 overview, backward pass).
 // Partitioning (same overview): one workgroup per block of key columns of one
-// (batch, head); it sweeps the query row blocks, keeps its dK and dV on chip,
-// and merges dQ, the only quantity shared between column blocks, by atomic
-// addition into a float32 accumulator.
+// (batch, head); it sweeps the query row blocks and keeps its dK and dV on chip.
+// dQ, the one quantity the key blocks share, is computed by its own pass
+// (fa_bwd_dq.hip) instead of being merged by atomics here.
 //
 // The gradients are the chain rule through the softmax (the pages only name
 // it): dP = dO V^T, D_i = sum_j P_ij dP_ij = dO_i . O_i, dS = P o (dP - D),
 // dV = P^T dO, dK = scale dS^T Q, dQ = scale dS K.
 //
-// Layout work done once per call (preprocess kernel): D_i, a zeroed float32 dQ
-// accumulator, and transposed copies Q^T and dO^T ([d][rows], rows padded to a
-// multiple of 64). In the transposed copies the rows of every 16-row group are
-// stored in the order 0-3, 8-11, 4-7, 12-15: eight consecutive positions then
-// hold exactly the rows that one half of a wave holds in an MFMA accumulator
-// (rows 4h..4h+3 and 8+4h..8+4h+3), so the dK/dV products read their Q^T/dO^T
-// operand with plain 16-byte LDS reads instead of transposing 8-byte reads.
+// Layout work done once per call (preprocess kernel): D_i and transposed copies
+// Q^T and dO^T ([d][rows], rows padded to a multiple of 64). In the transposed
+// copies the rows of every 16-row group are stored in the order 0-3, 8-11,
+// 4-7, 12-15: eight consecutive positions then hold exactly the rows that one
+// half of a wave holds in an MFMA accumulator (rows 4h..4h+3 and 8+4h..8+4h+3),
+// so the dK/dV products read their Q^T/dO^T operand with plain 16-byte LDS
+// reads instead of transposing 8-byte reads.
 //
-// Main kernel, per workgroup of 4 waves = 128 keys; wave w owns keys
+// dK/dV kernel, per workgroup of 4 waves = 128 keys; wave w owns keys
 // key0 + 32w .. +31. Per block of BM query rows, per wave:
 //   S  = Q K_w^T, dP = dO V_w^T   MFMA 32x32x16; Q/dO rows from LDS, K_w/V_w in
 //                                 VGPRs. Each lane holds one key column.
@@ -28,9 +28,6 @@
 //   dS = P o (dP - D_i)
 //   dV_w^T += dO^T P, dK_w^T += Q^T dS    P, dS straight from registers as the
 //                                 B operand, dO^T/Q^T by 16-byte LDS reads
-//   dS^T -> LDS; then wave w computes one 32x32 tile of dQ = dS K over all 128
-//   keys (dS by transposing LDS reads, its K columns held in VGPRs since the
-//   start) and adds it atomically to the float32 accumulator.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -45,21 +42,21 @@ __device__ __forceinline__ int perm16(int pos) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Preprocess: D_i = sum_c dO_ic O_ic, zero the dQ accumulator, write Q^T and dO^T.
+// Preprocess: D_i = sum_c dO_ic O_ic, and the transposed copies Q^T and dO^T.
 
-constexpr int kPreRows = 64;  // rows per preprocess workgroup; also the row padding of Q^T/dO^T
+constexpr int kPreRows = 64;   // rows per preprocess workgroup
+constexpr int kRowPad = 128;   // Q^T / dO^T rows are padded to a multiple of this (>= any BM)
 
 struct PreParams {
   const bf16* q;
   const bf16* o;
   const bf16* dout;
   float* dvec;
-  float* dqacc;
   bf16* qt;
   bf16* dot;
   int BH;
   int N;
-  int Np;   // padded row count of Q^T / dO^T (multiple of kPreRows)
+  int Np;   // padded row count of Q^T / dO^T (multiple of kRowPad)
 };
 
 template <int D>
@@ -95,9 +92,6 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(PreParams p) {
       const bf16x8 b = __builtin_bit_cast(bf16x8, xg);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
-      f32x4* z = reinterpret_cast<f32x4*>(p.dqacc + off);
-      z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // The LPR lanes of one row are consecutive: reduce across them.
 #pragma unroll
@@ -108,7 +102,8 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(PreParams p) {
   }
   __syncthreads();
 
-  // Transposed, row-permuted copies: output chunk (column c, positions 8j..8j+7).
+  // Transposed, row-permuted copies: output chunk (column c, positions 8j..8j+7);
+  // positions past N (up to the padding) are written as zeros.
 #pragma unroll
   for (int t = 0; t < TI; ++t) {
     const int id = tid + 256 * t;
@@ -128,50 +123,30 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(PreParams p) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Finish: dq = bf16(scale * dQ accumulator).
-
-__global__ __launch_bounds__(256) void fa_bwd_finish_kernel(const float* __restrict__ dqacc,
-                                                            bf16* __restrict__ dq, float scale,
-                                                            int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = reinterpret_cast<const f32x4*>(dqacc)[2 * i];
-  const f32x4 b = reinterpret_cast<const f32x4*>(dqacc)[2 * i + 1];
-  reinterpret_cast<bf16x8*>(dq)[i] = to_bf16x8(a[0] * scale, a[1] * scale, a[2] * scale,
-                                               a[3] * scale, b[0] * scale, b[1] * scale,
-                                               b[2] * scale, b[3] * scale);
-}
-
-// ------------------------------------------------------------------------------------------------
-// Main backward kernel.
+// dK/dV kernel.
 
 template <int D>
 struct BwdCfg {
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BN = 32 * WAVES;           // keys per workgroup (= block-mask granularity)
-  static constexpr int BM = D == 128 ? 32 : 64;   // query rows per iteration
+  static constexpr int BM = D == 128 ? 64 : 128;  // query rows per iteration
   static constexpr int IT = BM / 32;              // 32-row sub-tiles
   static constexpr int RS = BM / 16;              // 16-row MFMA k-steps
   static constexpr int KS = D / 16;               // 16-column MFMA k-steps over the head dim
   static constexpr int CT = D / 32;               // 32-column sub-tiles of the head dim
-  static constexpr int QS = BN / 16;              // 16-key MFMA k-steps of dQ = dS K
-  // LDS row strides (bf16 elements), each chosen so that its access pattern is
-  // free of bank conflicts: 16-byte row reads of 32 rows (Q, dO, Q^T, dO^T),
-  // 8-byte writes / transposing reads (dS^T), transposing reads (K, set-up).
+  // LDS row strides (bf16 elements): 16-byte row reads of 32 rows are free of
+  // bank conflicts at a stride of 4 (mod 64) dwords (Q, dO: 136 / 72 elements,
+  // Q^T, dO^T: 72 / 136 elements).
   static constexpr int STRQ = D + 8;              // Q, dO tiles     [BM][STRQ]
   static constexpr int STRT = BM + 8;             // Q^T, dO^T tiles [D][STRT]
-  static constexpr int STRS = BM + 4;             // dS^T            [BN][STRS]
-  static constexpr int STRK = D + 32;             // K block         [BN][STRK] (set-up only)
   static constexpr int QTILE = BM * STRQ;
   static constexpr int TTILE = D * STRT;
   static constexpr int STAGE = 2 * QTILE + 2 * TTILE;
   static constexpr int CH = BM * D / 8;           // 16-byte chunks per tile (all four tiles)
   static constexpr int CPT = CH / THREADS;
-  static_assert(CT * IT == WAVES, "one 32x32 dQ tile per wave");
   static_assert(CH % THREADS == 0, "tiles split evenly over threads");
-  static_assert(BN * STRK <= 2 * STAGE, "K block fits in the stage buffers");
-  static_assert(kPreRows % BM == 0, "row padding of the transposed copies covers whole row blocks");
+  static_assert(kRowPad % BM == 0, "row padding of the transposed copies covers whole row blocks");
 };
 
 struct BwdParams {
@@ -183,7 +158,6 @@ struct BwdParams {
   const bf16* dot;
   const float* lse;
   const float* dvec;
-  float* dqacc;
   bf16* dk;
   bf16* dv;
   int BH;
@@ -197,11 +171,10 @@ struct BwdParams {
 };
 
 template <int D, bool CAUSAL, bool BLOCK>
-__global__ __launch_bounds__(256) void fa_bwd_main_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 tiles[2 * C::STAGE];  // [stage][Q, dO, Q^T, dO^T]
   __shared__ __attribute__((aligned(16))) float rowstat[2][2][C::BM]; // [stage][LSE*log2e, D][row]
-  __shared__ __attribute__((aligned(16))) bf16 dSt[C::BN * C::STRS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -223,38 +196,10 @@ __global__ __launch_bounds__(256) void fa_bwd_main_kernel(BwdParams p) {
   const bf16* __restrict__ dOTh = p.dot + (int64_t)bh * D * p.Np;
   const float* __restrict__ Lh = p.lse + (int64_t)bh * N;
   const float* __restrict__ Dh = p.dvec + (int64_t)bh * N;
-  float* __restrict__ dQh = p.dqacc + head;
 
   const int key0 = kb * C::BN;
   const int wkey0 = key0 + 32 * wave;
   const int mykey = wkey0 + l32;   // this lane's key column
-  const int itq = wave / C::CT;    // this wave's dQ tile: rows 32*itq.., columns 32*ctq..
-  const int ctq = wave % C::CT;
-
-  // dQ's B operand: K[16ks + 8hh .. +7][32ctq + l32], through a transposing read
-  // of the K block staged in LDS. Keys past N are clamped (their dS is zero).
-  bf16x8 ktf[C::QS];
-  {
-    bf16* Ks = tiles;
-#pragma unroll
-    for (int c = 0; c < C::BN * D / 8 / C::THREADS; ++c) {
-      const int id = tid + c * C::THREADS;
-      const int r = id / (D / 8);
-      const int col = (id % (D / 8)) * 8;
-      const int key = min(key0 + r, N - 1);
-      *reinterpret_cast<u32x4*>(Ks + r * C::STRK + col) =
-          *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + col);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < C::QS; ++ks) {
-      const int r0 = 16 * ks + 8 * hh + (i16 >> 2);
-      const int c0 = 32 * ctq + 16 * (g16 & 1) + 4 * (i16 & 3);
-      ktf[ks] = cat(lds_tr(Ks + r0 * C::STRK + c0), lds_tr(Ks + (r0 + 4) * C::STRK + c0));
-    }
-    __syncthreads();  // the staging area becomes the row-block buffers
-  }
-
   // S / dP B operands: K and V rows of this lane's key, k = head-dim chunks.
   bf16x8 kf[C::KS], vf[C::KS];
   {
@@ -393,12 +338,6 @@ __global__ __launch_bounds__(256) void fa_bwd_main_kernel(BwdParams p) {
       dsk[2 * it] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
       dsk[2 * it + 1] =
           to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
-      // dS^T row (key) of this lane, four consecutive query rows per store.
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        *reinterpret_cast<bf16x4*>(dSt + (32 * wave + l32) * C::STRS + 32 * it + 8 * g + 4 * hh) =
-            to_bf16x4(dsv[4 * g], dsv[4 * g + 1], dsv[4 * g + 2], dsv[4 * g + 3]);
-      }
     }
 
     // dV^T += dO^T P and dK^T += Q^T dS; the permuted row order of the transposed
@@ -412,24 +351,6 @@ __global__ __launch_bounds__(256) void fa_bwd_main_kernel(BwdParams p) {
         const bf16x8 qt = lds_b128(QTs + (32 * ct + l32) * C::STRT + 16 * ks + 8 * hh);
         dk[ct] = mfma32(qt, dsk[ks], dk[ct]);
       }
-    }
-    __syncthreads();   // dS^T complete
-
-    // dQ[rows 32itq..][cols 32ctq..] += sum over the 128 keys of dS[row][key] K[key][col].
-    f32x16 acc = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < C::QS; ++ks) {
-      const int r0 = 16 * ks + 8 * hh + (i16 >> 2);
-      const int c0 = 32 * itq + 16 * (g16 & 1) + 4 * (i16 & 3);
-      const bf16x8 a = cat(lds_tr(dSt + r0 * C::STRS + c0), lds_tr(dSt + (r0 + 4) * C::STRS + c0));
-      acc = mfma32(a, ktf[ks], acc);
-    }
-    // acc[v]: row row0 + 32*itq + 8*(v/4) + 4*hh + v%4, column 32*ctq + l32. Rows
-    // past N have dS = 0, so their (exactly zero) sums go to row N-1 unchanged.
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = min(row0 + 32 * itq + 8 * (v / 4) + 4 * hh + (v % 4), N - 1);
-      unsafeAtomicAdd(dQh + (int64_t)row * D + 32 * ctq + l32, acc[v]);
     }
   };
 
@@ -445,7 +366,7 @@ __global__ __launch_bounds__(256) void fa_bwd_main_kernel(BwdParams p) {
       if (rn < n_rb) load_rb(rn);
       compute(rb, buf);
       if (rn < n_rb) store_rb(buf ^ 1);
-      __syncthreads();   // next block staged; dS^T and this block's buffers free
+      __syncthreads();   // next block staged; this block's buffers free
       buf ^= 1;
       rb = rn;
     }
@@ -471,7 +392,7 @@ __global__ __launch_bounds__(256) void fa_bwd_main_kernel(BwdParams p) {
 }
 
 template <int D>
-hipError_t launch_main_d(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t stream) {
   using C = BwdCfg<D>;
   BwdParams p;
   p.q = static_cast<const bf16*>(a.q);
@@ -482,7 +403,6 @@ hipError_t launch_main_d(const BwdArgs& a, hipStream_t stream) {
   p.dot = static_cast<const bf16*>(a.dot);
   p.lse = a.lse;
   p.dvec = a.dvec;
-  p.dqacc = a.dqacc;
   p.dk = static_cast<bf16*>(a.dk);
   p.dv = static_cast<bf16*>(a.dv);
   p.BH = a.BH;
@@ -499,21 +419,21 @@ hipError_t launch_main_d(const BwdArgs& a, hipStream_t stream) {
   const bool blk = a.mask.blocks != nullptr;
   if (a.mask.causal) {
     if (blk)
-      hipLaunchKernelGGL((fa_bwd_main_kernel<D, true, true>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, true, true>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((fa_bwd_main_kernel<D, true, false>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, true, false>), grid, block, 0, stream, p);
   } else {
     if (blk)
-      hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, true>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, false, true>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((fa_bwd_main_kernel<D, false, false>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, false, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-int bwd_row_padding() { return kPreRows; }
+int bwd_row_padding() { return kRowPad; }
 
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream) {
   PreParams p;
@@ -521,7 +441,6 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream) {
   p.o = static_cast<const bf16*>(a.o);
   p.dout = static_cast<const bf16*>(a.dout);
   p.dvec = a.dvec;
-  p.dqacc = a.dqacc;
   p.qt = static_cast<bf16*>(a.qt);
   p.dot = static_cast<bf16*>(a.dot);
   p.BH = a.BH;
@@ -535,16 +454,8 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
-  return a.d == 128 ? launch_main_d<128>(a, stream) : launch_main_d<64>(a, stream);
-}
-
-hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {
-  const int64_t n8 = (int64_t)a.BH * a.N * a.d / 8;
-  const dim3 grid((unsigned)((n8 + 255) / 256));
-  hipLaunchKernelGGL(fa_bwd_finish_kernel, grid, dim3(256), 0, stream, a.dqacc,
-                     static_cast<bf16*>(a.dq), a.scale, n8);
-  return hipGetLastError();
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
+  return a.d == 128 ? launch_dkdv_d<128>(a, stream) : launch_dkdv_d<64>(a, stream);
 }
 
 }  // namespace fa

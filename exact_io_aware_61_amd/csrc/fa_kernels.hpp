@@ -39,7 +39,6 @@ struct BwdArgs {
   float scale;
   MaskArgs mask;
   float* dvec;   // workspace: D_i [BH * N]
-  float* dqacc;  // workspace: fp32 dQ accumulator [BH * N * d]
   void* qt;      // workspace: Q^T, bf16 [BH][d][Np], rows permuted within 16-row groups
   void* dot;     // workspace: dO^T, same layout
   int Np;        // N rounded up to bwd_row_padding()
@@ -50,7 +49,7 @@ int bwd_row_padding();
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace fa

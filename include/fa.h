@@ -13,8 +13,9 @@
  *   - FlashAttention-2 overview (jishu.shishitao.com), "main operations": the
  *     backward needs only the row logsumexp; the forward gives each worker one
  *     block of query rows; the backward gives each worker one block of key
- *     columns and merges dQ by atomic addition; block-sparse attention skips
- *     zero blocks ("Block-Sparse FlashAttention").
+ *     columns and merges dQ by atomic addition (here dQ has a pass of its own
+ *     instead, see fa_bwd); block-sparse attention skips zero blocks
+ *     ("Block-Sparse FlashAttention").
  *
  * Conventions shared by every entry point:
  *   Layout     Q, K, V, O, dO, dQ, dK, dV are [B, H, N, d] bfloat16, contiguous,
@@ -34,8 +35,7 @@
  *   Errors     argument checks run on the host before anything is enqueued and
  *              return a negative fa_status; nothing is written then. A failed
  *              kernel launch returns FA_ERR_HIP.
- *   Determinism fa_fwd, dK and dV are bitwise reproducible run to run; dQ is
- *              merged by floating-point atomics, so its low bits may vary.
+ *   Determinism every output is bitwise reproducible run to run (no atomics).
  */
 #ifndef EXACT_IO_AWARE_FA_H
 #define EXACT_IO_AWARE_FA_H
@@ -95,24 +95,25 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * Bytes of device workspace fa_bwd needs, written to *bytes (pure host
  * arithmetic). The workspace holds, each part 256-byte aligned: the row terms
- * D_i = dO_i . O_i ([B, H, N] float32), the float32 dQ accumulator
- * ([B, H, N, d]), and transposed bf16 copies of Q and dO ([B, H, d, Np] each,
- * Np = N rounded up to a multiple of 64).
+ * D_i = dO_i . O_i ([B, H, N] float32) and transposed bf16 copies of Q and dO
+ * ([B, H, d, Np] each, Np = N rounded up to a multiple of 128).
  */
 int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);
 
 /*
  * Backward: dQ, dK, dV of L given dO = dL/dO, recomputing P tile by tile from
- * q, k and the forward's lse (lecture summary, part 4.2; FlashAttention-2
- * overview, backward pass: one workgroup per block of key columns, dQ merged
- * across workgroups by atomic addition).
+ * q, k and the forward's lse (lecture summary, part 4.2). dK and dV come from
+ * one workgroup per block of key columns (FlashAttention-2 overview, backward
+ * pass); dQ, the only quantity those workgroups share, comes from its own pass
+ * over blocks of query rows instead of an atomic merge, so every output is
+ * bitwise reproducible.
  *   q, k, v, o, dout : inputs [B, H, N, d] bf16 (o from fa_fwd with the same arguments)
  *   lse              : input [B, H, N] float32 from fa_fwd
  *   dq, dk, dv       : outputs [B, H, N, d] bf16
  *   workspace        : DEVICE buffer of at least fa_bwd_workspace_size() bytes,
  *                      owned by the caller; its contents on entry do not matter
  *                      and are overwritten.
- * Enqueues three kernels: fa_bwd_preprocess, fa_bwd_main, fa_bwd_finish (below).
+ * Enqueues the three stages below, in order.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv,
@@ -122,23 +123,24 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 /*
  * The three stages of fa_bwd, exposed so a caller can time or schedule them
  * separately; calling them in order on one stream, with one workspace, equals
- * fa_bwd.
- *   fa_bwd_preprocess : D_i = sum_c dO_ic O_ic into the workspace, zeroes the
- *                       float32 dQ accumulator, and writes the transposed
- *                       copies of Q and dO.
- *   fa_bwd_main       : dK, dV (written as bf16) and dQ accumulated in float32
- *                       in the workspace.
- *   fa_bwd_finish     : writes dq = bf16(scale * dQ accumulator).
+ * fa_bwd (dkdv and dq only read the workspace, so they may also run
+ * concurrently once fa_bwd_preprocess has finished).
+ *   fa_bwd_preprocess : D_i = sum_c dO_ic O_ic and the transposed copies of Q
+ *                       and dO, into the workspace.
+ *   fa_bwd_dkdv       : dK, dV (bf16).
+ *   fa_bwd_dq         : dQ (bf16).
  * Argument meanings and checks are those of fa_bwd.
  */
 int fa_bwd_preprocess(const void* q, const void* o, const void* dout, int B, int H, int N, int d,
                       void* workspace, size_t workspace_bytes, void* stream);
-int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                 const float* lse, void* dk, void* dv,
                 int B, int H, int N, int d, float scale, const fa_mask_t* mask,
                 void* workspace, size_t workspace_bytes, void* stream);
-int fa_bwd_finish(void* dq, int B, int H, int N, int d, float scale,
-                  void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+              const float* lse, void* dq,
+              int B, int H, int N, int d, float scale, const fa_mask_t* mask,
+              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* fa_strerror(int status);

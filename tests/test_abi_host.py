@@ -34,7 +34,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
-                            "fa_bwd_main", "fa_bwd_finish", "fa_strerror"])
+                            "fa_bwd_dkdv", "fa_bwd_dq", "fa_strerror"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -56,9 +56,8 @@ def test_workspace_size_arithmetic(lib):
     for B, H, N, d in [(2, 16, 8192, 128), (1, 1, 1, 64), (4, 16, 16384, 64), (3, 5, 1000, 128)]:
         assert lib.fa_bwd_workspace_size(B, H, N, d, ctypes.byref(n)) == OK
         r256 = lambda x: (x + 255) // 256 * 256
-        Np = (N + 63) // 64 * 64
-        assert n.value == (r256(B * H * N * 4) + r256(B * H * N * d * 4)
-                           + 2 * r256(B * H * d * Np * 2))
+        Np = (N + 127) // 128 * 128
+        assert n.value == r256(B * H * N * 4) + 2 * r256(B * H * d * Np * 2)
     assert lib.fa_bwd_workspace_size(1, 1, 1, 96, ctypes.byref(n)) == SHAPE
     assert lib.fa_bwd_workspace_size(-1, 1, 1, 64, ctypes.byref(n)) == SHAPE
     assert lib.fa_bwd_workspace_size(1, 1, 1, 64, None) == NULL
@@ -123,10 +122,18 @@ def test_bwd_rejects_bad_arguments(lib):
     assert bwd(dq=ctypes.c_void_p(0x10000 + 64)) == ALIAS   # dq overlaps q
     assert lib.fa_bwd_preprocess(None, P[1], P[2], 1, 2, 256, 64, ws, need, STREAM) == NULL
     assert lib.fa_bwd_preprocess(P[0], P[1], P[2], 1, 2, 256, 64, ws, need - 1, STREAM) == WS
-    assert lib.fa_bwd_main(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 2, 256, 64, 0.125, None,
+    assert lib.fa_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 2, 256, 64, 0.125, None,
                            ws, 16, STREAM) == WS
-    assert lib.fa_bwd_finish(P[5], 1, 2, 256, 64, 0.125, None, need, STREAM) == WS
-    assert lib.fa_bwd_finish(P[5], 1, 2, 256, 64, -1.0, ws, need, STREAM) == SCALE
+    assert lib.fa_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], None, P[6], 1, 2, 256, 64, 0.125, None,
+                           ws, need, STREAM) == NULL
+    assert lib.fa_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[0], P[6], 1, 2, 256, 64, 0.125, None,
+                           ws, need, STREAM) == ALIAS   # dk overlaps q
+    assert lib.fa_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], 1, 2, 256, 64, 0.125, None, None,
+                         need, STREAM) == WS
+    assert lib.fa_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], 1, 2, 256, 64, -1.0, None, ws, need,
+                         STREAM) == SCALE
+    assert lib.fa_bwd_dq(P[0], P[1], P[2], P[3], P[4], ctypes.c_void_p(0x60008), 1, 2, 256, 64,
+                         0.125, None, ws, need, STREAM) == ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

@@ -169,13 +169,14 @@ def test_gradient_sums():
     np.testing.assert_allclose(dv.sum(axis=2), dof.sum(axis=2), atol=0.05 * np.sqrt(512))
 
 
-def test_forward_and_dkdv_bitwise_reproducible():
-    q, k, v, do = make_qkv(2, 4, 1024, 128, seed=46)
+@pytest.mark.parametrize("d", [64, 128])
+def test_every_output_bitwise_reproducible(d):
+    """No atomics anywhere: repeated calls give identical bits for every output."""
+    q, k, v, do = make_qkv(2, 4, 1024, d, seed=46)
     a = run_gpu(q, k, v, do, causal=True, scale=0.088)
     b = run_gpu(q, k, v, do, causal=True, scale=0.088)
-    for key in ("o", "lse", "dk", "dv"):
+    for key in ("o", "lse", "dq", "dk", "dv"):
         assert torch.equal(a[key], b[key]), key
-    assert torch.allclose(a["dq"].float(), b["dq"].float(), atol=1e-2)
 
 
 def test_autograd_wrapper_matches_backward():
@@ -187,8 +188,7 @@ def test_autograd_wrapper_matches_backward():
     o2, lse = fa.forward(q, k, v, causal=True)
     dq, dk, dv = fa.backward(q, k, v, o2, lse, do, causal=True)
     assert torch.equal(o, o2)
-    assert torch.equal(kr.grad, dk) and torch.equal(vr.grad, dv)
-    assert torch.allclose(qr.grad.float(), dq.float(), atol=1e-2)
+    assert torch.equal(kr.grad, dk) and torch.equal(vr.grad, dv) and torch.equal(qr.grad, dq)
 
 
 # -------------------------------------------------------------------------------------------------
