@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "fa.h"
+#include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
 namespace {
@@ -43,6 +44,7 @@ int check_mask(const fa_mask_t* m, const Shape& s, fa::MaskArgs* out) {
   out->causal = (m->kind & FA_MASK_CAUSAL) != 0;
   if (m->kind & FA_MASK_BLOCK) {
     if (m->block != 128 || m->blocks == nullptr || m->bh_stride < 0) return FA_ERR_MASK;
+    if (out->nb > fa::kMaxMaskBlocks) return FA_ERR_MASK;
     out->blocks = m->blocks;
     out->bh_stride = m->bh_stride;
   }

@@ -70,3 +70,72 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 }  // namespace fa
+
+namespace fa {
+
+// ------------------------------------------------------------------------------------------------
+// Swizzled LDS tiles filled by direct global->LDS loads.
+//
+// A tile has rows of C 16-byte chunks (C = 8 or 16), stored without padding;
+// chunk c of row r sits at chunk position c ^ swz<C>(r). The permutation makes
+// both access patterns of the kernels free of LDS bank conflicts: 16-byte reads
+// of 16 consecutive rows at one chunk (MFMA operands read along the row) and
+// transposing 8-byte reads of 4 consecutive rows x 4 consecutive chunks.
+template <int C>
+__device__ __forceinline__ int swz(int r);
+template <>
+__device__ __forceinline__ int swz<16>(int r) {
+  return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+template <>
+__device__ __forceinline__ int swz<8>(int r) {
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Element offset of (row r, column col) in a swizzled tile with rows of C chunks.
+template <int C>
+__device__ __forceinline__ int toff(int r, int col) {
+  return r * (8 * C) + ((((col >> 3) ^ swz<C>(r)) & (C - 1)) << 3) + (col & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane
+// l writes LDS bytes [lds + 16 l, lds + 16 l + 16). Issued through asm so that
+// the compiler does not treat it as an LDS store and add waits before later
+// LDS reads of other buffers; the kernels order these loads themselves (wait
+// for the vector-memory counter, then a workgroup barrier, before any read).
+__device__ __forceinline__ void dma16(const void* src, const bf16* lds_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds_dst));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+
+// One 1 KiB slot of a swizzled tile: lane l fills chunk position 64*slot + l,
+// fetching the chunk of the source row that the swizzle stores there.
+// row_ptr(r) returns the global address of tile row r.
+template <int C, typename RowPtr>
+__device__ __forceinline__ void dma_slot(bf16* tile, int slot, int lane, RowPtr row_ptr) {
+  const int pos = slot * 64 + lane;
+  const int r = pos / C;
+  const int c = (pos % C) ^ swz<C>(r);
+  dma16(row_ptr(r) + 8 * c, tile + slot * 512);
+}
+
+// Block-mask bits staged in LDS: one 128-row mask row (or column) is at most
+// kMaxMaskBlocks entries, so N <= 128 * kMaxMaskBlocks when a block mask is used.
+constexpr int kMaxMaskBlocks = 16384;
+constexpr int kMaskWords = kMaxMaskBlocks / 32;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt low bits [3:0], high bits [15:14]; expcnt and lgkmcnt at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+}  // namespace fa

@@ -6,7 +6,9 @@
 // query rows of one (batch, head) and sweeps the key/value tiles, so no
 // workgroup talks to another. Inside the workgroup every wave owns 32 query
 // rows (the "split-Q" partition of the same overview): K/V tiles are shared
-// through LDS, and no partial results are exchanged between waves.
+// through LDS, and no partial results are exchanged between waves. Tiles reach
+// LDS by direct global->LDS loads (no staging registers), three tiles in
+// flight, in the swizzled layout of fa_common.hpp.
 //
 // Per wave and K/V tile (BN keys):
 //   S^T = K_tile Q_wave^T       MFMA 32x32x16, K read from LDS, Q^T held in VGPRs.
@@ -38,25 +40,21 @@ namespace {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;           // query rows per workgroup
   static constexpr int BN = 64;                   // keys per K/V tile
-  // LDS row strides in bf16 elements. K is read with 16-byte row reads of 32
-  // consecutive rows: a stride of 4 (mod 64) dwords spreads them over all 64
-  // banks. V is read with the transposing 8-byte read of 8 rows x 64 bytes: a
-  // stride of 16 (mod 64) dwords puts four consecutive rows on disjoint banks.
-  static constexpr int STRK = D + 8;              // 136 / 72
-  static constexpr int STRV = D + 32;             // 160 / 96
+  static constexpr int C = D / 8;                 // 16-byte chunks per tile row
   static constexpr int KS = D / 16;               // MFMA k-steps over the head dim
   static constexpr int NT = BN / 32;              // 32-key sub-tiles of S^T
   static constexpr int CT = D / 32;               // 32-column sub-tiles of O^T
-  static constexpr int CHUNKS = BN * D / 8;       // 16-byte pieces per K or V tile
-  static constexpr int CPT = CHUNKS / THREADS;    // ... per thread
-  static constexpr int KTILE = BN * STRK;         // elements per LDS K tile
-  static constexpr int VTILE = BN * STRV;         // elements per LDS V tile
-  static constexpr int STAGE = KTILE + VTILE;
-  static_assert(CHUNKS % THREADS == 0, "tile must split evenly over threads");
+  static constexpr int TILE = BN * D;             // elements per K or V tile (swizzled, unpadded)
+  static constexpr int STAGE = 2 * TILE;          // K tile, V tile
+  static constexpr int NSTAGE = 3;                // tiles in flight: two loading, one in use
+  static constexpr int SLOTS = BN * C / 64;       // 1 KiB direct-load slots per tile
+  static constexpr int SPW = SLOTS / WAVES;       // ... per wave
+  static constexpr int LPT = 2 * SPW;             // direct loads per thread per K+V tile
+  static_assert(SLOTS % WAVES == 0, "tile slots split evenly over waves");
 };
 
 // Reference-max moves happen only when a row max exceeds it by more than this
@@ -79,10 +77,10 @@ struct FwdParams {
 };
 
 template <int D, bool CAUSAL, bool BLOCK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_kernel(FwdParams p) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];  // [buffer][K tile, V tile]
+  __shared__ __attribute__((aligned(16))) bf16 smem[C::NSTAGE * C::STAGE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,9 +106,34 @@ void fa_fwd_kernel(FwdParams p) {
 
   int kt_end = (N + C::BN - 1) / C::BN;
   if (CAUSAL) kt_end = min(kt_end, (row0 + C::BM - 1) / C::BN + 1);
-  const uint8_t* mrow = nullptr;
-  if (BLOCK) mrow = p.blocks + bh * p.blocks_bh_stride + (int64_t)(row0 / 128) * p.nb;
-  auto kept = [&](int kt) -> bool { return !BLOCK || mrow[(kt * C::BN) / 128] != 0; };
+
+  // Block mask: the workgroup's rows span two 128-row mask rows; their bits go
+  // to LDS once (so the tile loop reads no global memory besides the tiles). A
+  // tile is loaded if either row keeps it; a wave skips tiles its row drops.
+  __shared__ uint32_t mbits[BLOCK ? 2 * kMaskWords : 1];
+  const int mr0 = row0 / 128;
+  const int my_mr = wrow0 / 128 - mr0;   // this wave's mask row: 0 or 1
+  if (BLOCK) {
+    const int nw = (p.nb + 63) / 64;
+    const uint8_t* grid = p.blocks + bh * p.blocks_bh_stride;
+    for (int j = wave; j < 2 * nw; j += C::WAVES) {
+      const int rr = j / nw;
+      const int b = (j % nw) * 64 + lane;
+      const bool keep = mr0 + rr < p.nb && b < p.nb && grid[(int64_t)(mr0 + rr) * p.nb + b] != 0;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+      if (lane == 0) {
+        mbits[rr * kMaskWords + 2 * (j % nw)] = (uint32_t)bal;
+        mbits[rr * kMaskWords + 2 * (j % nw) + 1] = (uint32_t)(bal >> 32);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  auto mbit = [&](int rr, int kt) -> bool {
+    const int b = (kt * C::BN) / 128;
+    return (mbits[rr * kMaskWords + (b >> 5)] >> (b & 31)) & 1u;
+  };
+  auto kept = [&](int kt) -> bool { return !BLOCK || mbit(0, kt) || mbit(1, kt); };
   auto next_kept = [&](int kt) -> int {
     ++kt;
     while (kt < kt_end && !kept(kt)) ++kt;
@@ -127,30 +150,34 @@ void fa_fwd_kernel(FwdParams p) {
       qf[kk] = bf16x8{};
   }
 
-  u32x4 kst[C::CPT], vst[C::CPT];  // staging registers for the next tile
-  auto load_tile = [&](int kt) {
+  // Direct global->LDS loads of one K/V tile into a stage; keys past N are
+  // clamped to N-1 (they are masked, any valid row will do).
+  auto issue = [&](int kt, int stage) {
+    bf16* Ks = smem + stage * C::STAGE;
+    bf16* Vs = Ks + C::TILE;
+    const int key0 = kt * C::BN;
 #pragma unroll
-    for (int c = 0; c < C::CPT; ++c) {
-      const int id = tid + c * C::THREADS;
-      const int r = id / (D / 8);
-      const int col = (id % (D / 8)) * 8;
-      const int key = min(kt * C::BN + r, N - 1);  // rows past N are masked; any valid row will do
-      kst[c] = *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + col);
-      vst[c] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + col);
+    for (int i = 0; i < C::SPW; ++i) {
+      const int slot = wave + i * C::WAVES;
+      dma_slot<C::C>(Ks, slot, lane,
+                     [&](int r) { return Kh + (int64_t)min(key0 + r, N - 1) * D; });
+      dma_slot<C::C>(Vs, slot, lane,
+                     [&](int r) { return Vh + (int64_t)min(key0 + r, N - 1) * D; });
     }
   };
-  auto store_tile = [&](int buf) {
-    bf16* Ks = smem + buf * C::STAGE;
-    bf16* Vs = Ks + C::KTILE;
+
+  // Lane offsets inside a K / V tile. The swizzle term depends only on the lane
+  // and on the k-step (K) or column sub-tile (V); the remaining steps (32-key
+  // sub-tile of K, 16-key step of V) add compile-time constants.
+  int koff[C::KS], voff[C::CT][2];
 #pragma unroll
-    for (int c = 0; c < C::CPT; ++c) {
-      const int id = tid + c * C::THREADS;
-      const int r = id / (D / 8);
-      const int col = (id % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Ks + r * C::STRK + col) = kst[c];
-      *reinterpret_cast<u32x4*>(Vs + r * C::STRV + col) = vst[c];
-    }
-  };
+  for (int kk = 0; kk < C::KS; ++kk) koff[kk] = toff<C::C>(l32, 16 * kk + 8 * hh);
+#pragma unroll
+  for (int ct = 0; ct < C::CT; ++ct) {
+    const int n0 = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
+    voff[ct][0] = toff<C::C>(4 * hh + (i16 >> 2), n0);
+    voff[ct][1] = toff<C::C>(8 + 4 * hh + (i16 >> 2), n0);
+  }
 
   f32x16 oacc[C::CT];
 #pragma unroll
@@ -160,12 +187,14 @@ void fa_fwd_kernel(FwdParams p) {
   float lb_run = 0.f;       // the same sum over the bf16-rounded probabilities
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-  auto compute = [&](int kt, int buf) {
-    const bf16* Ks = smem + buf * C::STAGE;
-    const bf16* Vs = Ks + C::KTILE;
+  auto compute = [&](int kt, int stage) {
+    const bf16* Ks = smem + stage * C::STAGE;
+    const bf16* Vs = Ks + C::TILE;
     const int kbase = kt * C::BN;
-    // Under the causal mask a wave whose rows all precede this tile sees none of it.
+    // Under the causal mask a wave whose rows all precede this tile sees none of
+    // it; under the block mask a wave skips the tiles its mask row drops.
     if (CAUSAL && kbase > wrow0 + 31) return;
+    if (BLOCK && !mbit(my_mr, kt)) return;
 
     f32x16 s[C::NT];
 #pragma unroll
@@ -174,7 +203,7 @@ void fa_fwd_kernel(FwdParams p) {
     for (int kk = 0; kk < C::KS; ++kk) {
 #pragma unroll
       for (int st = 0; st < C::NT; ++st) {
-        const bf16x8 a = lds_b128(Ks + (32 * st + l32) * C::STRK + 16 * kk + 8 * hh);
+        const bf16x8 a = lds_b128(Ks + koff[kk] + 32 * st * D);
         s[st] = mfma32(a, qf[kk], s[st]);
       }
     }
@@ -236,33 +265,40 @@ void fa_fwd_kernel(FwdParams p) {
     // 8+4hh..8+4hh+3, so the V^T operand is read as those two groups of four rows.
 #pragma unroll
     for (int ct = 0; ct < C::CT; ++ct) {
-      const int n0 = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
 #pragma unroll
       for (int ks = 0; ks < 2 * C::NT; ++ks) {
-        const int r0 = 16 * ks + 4 * hh + (i16 >> 2);
-        const i16x4 lo = lds_tr(Vs + r0 * C::STRV + n0);
-        const i16x4 hi = lds_tr(Vs + (r0 + 8) * C::STRV + n0);
+        const i16x4 lo = lds_tr(Vs + voff[ct][0] + 16 * ks * D);
+        const i16x4 hi = lds_tr(Vs + voff[ct][1] + 16 * ks * D);
         oacc[ct] = mfma32(cat(lo, hi), pk[ks], oacc[ct]);
       }
     }
   };
 
+  // Three-stage ring: while tile i is computed, tiles i+1 and i+2 are loading.
+  // At the top of each step a thread waits for its own loads of tile i, the
+  // barrier then publishes every thread's loads and guarantees that no wave
+  // still reads the stage the load of tile i+2 overwrites.
   int kt = 0;
   if (BLOCK && kt < kt_end && !kept(kt)) kt = next_kept(kt);
-  if (kt < kt_end) {
-    load_tile(kt);
-    store_tile(0);
+  int kn = kt < kt_end ? next_kept(kt) : kt_end;
+  if (kt < kt_end) issue(kt, 0);
+  // The Q operand loads above must be complete before the loop: a wait for
+  // them inside the loop would also wait for the tiles in flight.
+  wait_vmcnt<0>();
+  if (kn < kt_end) issue(kn, 1);
+  int stage = 0;
+  while (kt < kt_end) {
+    const int knn = kn < kt_end ? next_kept(kn) : kt_end;
+    if (kn < kt_end)
+      wait_vmcnt<C::LPT>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
-    int buf = 0;
-    while (kt < kt_end) {
-      const int kn = next_kept(kt);
-      if (kn < kt_end) load_tile(kn);
-      compute(kt, buf);
-      if (kn < kt_end) store_tile(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-      kt = kn;
-    }
+    if (knn < kt_end) issue(knn, stage == 0 ? 2 : stage - 1);
+    compute(kt, stage);
+    stage = stage == 2 ? 0 : stage + 1;
+    kt = kn;
+    kn = knn;
   }
 
   // Epilogue: combine the two lane halves' denominators, normalise once.

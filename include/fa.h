@@ -27,7 +27,8 @@
  *   Alignment  data pointers must be 16-byte aligned.
  *   Limits     B, H, N >= 0 (a zero extent is a no-op that returns FA_OK);
  *              d in {64, 128}; scale finite and > 0; B*H*N*d < 2^40.
- *              N need not be a multiple of any tile size.
+ *              N need not be a multiple of any tile size. With a block mask,
+ *              ceil(N / 128) <= 16384 (N <= 2^21).
  *   Streams    `stream` is a hipStream_t passed as void* (NULL = default
  *              stream). Every call only enqueues work and returns; results are
  *              ready after the caller synchronises the stream. Device faults
@@ -51,7 +52,7 @@ typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL                            */
   FA_ERR_SHAPE = -2,     /* B/H/N negative, d unsupported, or sizes overflow       */
-  FA_ERR_MASK = -3,      /* unknown mask kind, block != 128, or NULL block grid    */
+  FA_ERR_MASK = -3,      /* unknown mask kind, block != 128, NULL grid, N > 2^21  */
   FA_ERR_ALIGN = -4,     /* a data pointer is not 16-byte aligned                  */
   FA_ERR_WORKSPACE = -5, /* backward workspace missing or too small                */
   FA_ERR_HIP = -6,       /* the HIP runtime reported an error at launch            */
