@@ -135,17 +135,16 @@ struct BwdCfg {
   static constexpr int RS = BM / 16;              // 16-row MFMA k-steps
   static constexpr int KS = D / 16;               // 16-column MFMA k-steps over the head dim
   static constexpr int CT = D / 32;               // 32-column sub-tiles of the head dim
-  // LDS row strides (bf16 elements): 16-byte row reads of 32 rows are free of
-  // bank conflicts at a stride of 4 (mod 64) dwords (Q, dO: 136 / 72 elements,
-  // Q^T, dO^T: 72 / 136 elements).
-  static constexpr int STRQ = D + 8;              // Q, dO tiles     [BM][STRQ]
-  static constexpr int STRT = BM + 8;             // Q^T, dO^T tiles [D][STRT]
-  static constexpr int QTILE = BM * STRQ;
-  static constexpr int TTILE = D * STRT;
-  static constexpr int STAGE = 2 * QTILE + 2 * TTILE;
-  static constexpr int CH = BM * D / 8;           // 16-byte chunks per tile (all four tiles)
-  static constexpr int CPT = CH / THREADS;
-  static_assert(CH % THREADS == 0, "tiles split evenly over threads");
+  // Four tiles per row block, swizzled and unpadded (fa_common.hpp), filled by
+  // direct global->LDS loads: Q, dO [BM][D] (rows of CQ chunks) and Q^T, dO^T
+  // [D][BM] (rows of CT_ chunks).
+  static constexpr int CQ = D / 8;
+  static constexpr int CTR = BM / 8;
+  static constexpr int TILE = BM * D;             // elements per tile (all four)
+  static constexpr int STAGE = 4 * TILE;
+  static constexpr int SLOTS = TILE / 512;        // 1 KiB slots per tile
+  static constexpr int SPW = SLOTS / WAVES;
+  static_assert(SLOTS % WAVES == 0, "tile slots split evenly over waves");
   static_assert(kRowPad % BM == 0, "row padding of the transposed copies covers whole row blocks");
 };
 
@@ -171,9 +170,11 @@ struct BwdParams {
 };
 
 template <int D, bool CAUSAL, bool BLOCK>
-__global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 tiles[2 * C::STAGE];  // [stage][Q, dO, Q^T, dO^T]
+  static_assert(2 * C::STAGE * 2 + 2 * 2 * C::BM * 4 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) float rowstat[2][2][C::BM]; // [stage][LSE*log2e, D][row]
 
   const int tid = threadIdx.x;
@@ -210,6 +211,17 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdParams p) {
       vf[kk] = *reinterpret_cast<const bf16x8*>(Vh + (int64_t)key * D + 16 * kk + 8 * hh);
     }
   }
+  // Complete these before the loop: a wait for them inside it would also wait
+  // for the row block in flight.
+  wait_vmcnt<0>();
+
+  // Lane offsets of the 16-byte row reads inside the tiles; the 32-row (Q, dO)
+  // or 32-column (Q^T, dO^T) sub-tile steps add compile-time constants.
+  int qoff[C::KS], toff_r[C::RS];
+#pragma unroll
+  for (int kk = 0; kk < C::KS; ++kk) qoff[kk] = toff<C::CQ>(l32, 16 * kk + 8 * hh);
+#pragma unroll
+  for (int ks = 0; ks < C::RS; ++ks) toff_r[ks] = toff<C::CTR>(l32, 16 * ks + 8 * hh);
 
   f32x16 dk[C::CT], dv[C::CT];
 #pragma unroll
@@ -221,9 +233,28 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdParams p) {
   // Row blocks: under causal, rows before key0 see none of these keys.
   const int n_rb = (N + C::BM - 1) / C::BM;
   const int rb_begin = CAUSAL ? key0 / C::BM : 0;
+  // Block mask: this workgroup's key block is one mask column; its bits go to
+  // LDS once, so the row-block loop reads no global memory besides its tiles.
+  __shared__ uint32_t mbits[BLOCK ? kMaskWords : 1];
+  if (BLOCK) {
+    const int nw = (p.nb + 63) / 64;
+    const uint8_t* grid = p.blocks + bh * p.blocks_bh_stride;
+    for (int j = wave; j < nw; j += C::WAVES) {
+      const int b = j * 64 + lane;
+      const bool keep = b < p.nb && grid[(int64_t)b * p.nb + kb] != 0;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+      if (lane == 0) {
+        mbits[2 * j] = (uint32_t)bal;
+        mbits[2 * j + 1] = (uint32_t)(bal >> 32);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
   auto kept = [&](int rb) -> bool {
     if (!BLOCK) return true;
-    return p.blocks[bh * p.blocks_bh_stride + (int64_t)((rb * C::BM) / 128) * p.nb + kb] != 0;
+    const int b = (rb * C::BM) / 128;
+    return (mbits[b >> 5] >> (b & 31)) & 1u;
   };
   auto next_kept = [&](int rb) -> int {
     ++rb;
@@ -231,52 +262,36 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdParams p) {
     return rb;
   };
 
-  u32x4 sq[C::CPT], sdo[C::CPT], sqt[C::CPT], sdot[C::CPT];
+  // Direct global->LDS loads of one row block's four tiles into a stage, and
+  // the row statistics into registers (their raw values: they are first used
+  // after the compute phase, so the loads stay in flight across it).
   float s_l = 0.f, s_d = 0.f;
   int row_next = 0;   // first row of the staged block
-  auto load_rb = [&](int rb) {
+  auto issue = [&](int rb, int buf) {
     const int row0 = rb * C::BM;
     row_next = row0;
+    bf16* Qs = tiles + buf * C::STAGE;
+    bf16* dOs = Qs + C::TILE;
+    bf16* QTs = dOs + C::TILE;
+    bf16* dOTs = QTs + C::TILE;
 #pragma unroll
-    for (int c = 0; c < C::CPT; ++c) {
-      const int id = tid + c * C::THREADS;
-      const int r = id / (D / 8);
-      const int col = (id % (D / 8)) * 8;
-      const int64_t off = (int64_t)min(row0 + r, N - 1) * D + col;  // rows past N get P = 0
-      sq[c] = *reinterpret_cast<const u32x4*>(Qh + off);
-      sdo[c] = *reinterpret_cast<const u32x4*>(dOh + off);
-      const int dd = id / (C::BM / 8);
-      const int j = id % (C::BM / 8);
-      const int64_t toff = (int64_t)dd * p.Np + row0 + 8 * j;
-      sqt[c] = *reinterpret_cast<const u32x4*>(QTh + toff);
-      sdot[c] = *reinterpret_cast<const u32x4*>(dOTh + toff);
+    for (int i = 0; i < C::SPW; ++i) {
+      const int slot = wave + i * C::WAVES;
+      // rows past N are clamped: their P is 0 (LSE = +inf below)
+      dma_slot<C::CQ>(Qs, slot, lane,
+                      [&](int r) { return Qh + (int64_t)min(row0 + r, N - 1) * D; });
+      dma_slot<C::CQ>(dOs, slot, lane,
+                      [&](int r) { return dOh + (int64_t)min(row0 + r, N - 1) * D; });
+      dma_slot<C::CTR>(QTs, slot, lane, [&](int r) { return QTh + (int64_t)r * p.Np + row0; });
+      dma_slot<C::CTR>(dOTs, slot, lane, [&](int r) { return dOTh + (int64_t)r * p.Np + row0; });
     }
-    // Raw values only: they are first used after the compute phase, so the
-    // loads stay in flight across it (using them here would wait for every
-    // load issued above).
     if (tid < C::BM) {
       const int row = min(row0 + tid, N - 1);
       s_l = Lh[row];
       s_d = Dh[row];
     }
   };
-  auto store_rb = [&](int buf) {
-    bf16* Qs = tiles + buf * C::STAGE;
-    bf16* dOs = Qs + C::QTILE;
-    bf16* QTs = dOs + C::QTILE;
-    bf16* dOTs = QTs + C::TTILE;
-#pragma unroll
-    for (int c = 0; c < C::CPT; ++c) {
-      const int id = tid + c * C::THREADS;
-      const int r = id / (D / 8);
-      const int col = (id % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Qs + r * C::STRQ + col) = sq[c];
-      *reinterpret_cast<u32x4*>(dOs + r * C::STRQ + col) = sdo[c];
-      const int dd = id / (C::BM / 8);
-      const int j = id % (C::BM / 8);
-      *reinterpret_cast<u32x4*>(QTs + dd * C::STRT + 8 * j) = sqt[c];
-      *reinterpret_cast<u32x4*>(dOTs + dd * C::STRT + 8 * j) = sdot[c];
-    }
+  auto store_stats = [&](int buf) {
     if (tid < C::BM) {
       // +inf: the row contributes nothing (past N, or no visible key at all).
       const bool live = row_next + tid < N && s_l != -INFINITY;
@@ -287,34 +302,47 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdParams p) {
 
   auto compute = [&](int rb, int buf) {
     const bf16* Qs = tiles + buf * C::STAGE;
-    const bf16* dOs = Qs + C::QTILE;
-    const bf16* QTs = dOs + C::QTILE;
-    const bf16* dOTs = QTs + C::TTILE;
+    const bf16* dOs = Qs + C::TILE;
+    const bf16* QTs = dOs + C::TILE;
+    const bf16* dOTs = QTs + C::TILE;
     const float* Ls = rowstat[buf][0];
     const float* Ds = rowstat[buf][1];
     const int row0 = rb * C::BM;
 
-    f32x16 s[C::IT], dp[C::IT];
-#pragma unroll
-    for (int it = 0; it < C::IT; ++it) {
-      s[it] = f32x16{};
-      dp[it] = f32x16{};
-    }
-#pragma unroll
-    for (int kk = 0; kk < C::KS; ++kk) {
-#pragma unroll
-      for (int it = 0; it < C::IT; ++it) {
-        const bf16x8 a = lds_b128(Qs + (32 * it + l32) * C::STRQ + 16 * kk + 8 * hh);
-        s[it] = mfma32(a, kf[kk], s[it]);
-        const bf16x8 b = lds_b128(dOs + (32 * it + l32) * C::STRQ + 16 * kk + 8 * hh);
-        dp[it] = mfma32(b, vf[kk], dp[it]);
-      }
-    }
-    // s[it][v]: row row0 + 32*it + 8*(v/4) + 4*hh + v%4, key mykey.
     const bool edge = (CAUSAL && row0 < wkey0 + 31) || (key0 + C::BN > N);
-    bf16x8 pk[C::RS], dsk[C::RS];
+    // One 32-row sub-tile at a time (S, dP, softmax, then its share of dV/dK):
+    // the same LDS reads as a whole-block pass, with half the live registers.
 #pragma unroll
     for (int it = 0; it < C::IT; ++it) {
+      // All operand reads of the sub-tile are issued before its MFMAs (the
+      // scheduling barriers keep the compiler from pairing each read with its
+      // MFMA, which would expose the LDS latency once per MFMA).
+      bf16x8 qa[C::KS], ga[C::KS];
+#pragma unroll
+      for (int kk = 0; kk < C::KS; ++kk) {
+        qa[kk] = lds_b128(Qs + qoff[kk] + 32 * it * D);
+        ga[kk] = lds_b128(dOs + qoff[kk] + 32 * it * D);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < C::KS; ++kk) {
+        s = mfma32(qa[kk], kf[kk], s);
+        dp = mfma32(ga[kk], vf[kk], dp);
+      }
+      // Operands of this sub-tile's dV/dK products: read now, consumed after
+      // the softmax below.
+      bf16x8 ota[C::CT][2], qta[C::CT][2];
+#pragma unroll
+      for (int ct = 0; ct < C::CT; ++ct) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          ota[ct][h] = lds_b128(dOTs + toff_r[2 * it + h] + 32 * ct * C::BM);
+          qta[ct][h] = lds_b128(QTs + toff_r[2 * it + h] + 32 * ct * C::BM);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // s[v]: row row0 + 32*it + 8*(v/4) + 4*hh + v%4, key mykey.
       float pv[16], dsv[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -324,32 +352,31 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = 4 * g + r;
-          float pe = fast_exp2(__builtin_fmaf(s[it][v], p.sl2, -l4[r]));
+          float pe = fast_exp2(__builtin_fmaf(s[v], p.sl2, -l4[r]));
           if (edge) {
             const int row = row0 + rl + r;
             if ((CAUSAL && mykey > row) || mykey >= N) pe = 0.f;
           }
           pv[v] = pe;
-          dsv[v] = pe * (dp[it][v] - d4[r]);
+          dsv[v] = pe * (dp[v] - d4[r]);
         }
       }
-      pk[2 * it] = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-      pk[2 * it + 1] = to_bf16x8(pv[8], pv[9], pv[10], pv[11], pv[12], pv[13], pv[14], pv[15]);
-      dsk[2 * it] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-      dsk[2 * it + 1] =
-          to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
-    }
+      bf16x8 pk[2], dsk[2];
+      pk[0] = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+      pk[1] = to_bf16x8(pv[8], pv[9], pv[10], pv[11], pv[12], pv[13], pv[14], pv[15]);
+      dsk[0] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+      dsk[1] = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
 
-    // dV^T += dO^T P and dK^T += Q^T dS; the permuted row order of the transposed
-    // tiles makes positions 16ks + 8hh .. +7 the rows this lane half holds in P, dS.
+      // dV^T += dO^T P and dK^T += Q^T dS over this sub-tile's rows; the permuted
+      // row order of the transposed tiles makes positions 16ks + 8hh .. +7 the
+      // rows this lane half holds in P and dS.
 #pragma unroll
-    for (int ct = 0; ct < C::CT; ++ct) {
+      for (int ct = 0; ct < C::CT; ++ct) {
 #pragma unroll
-      for (int ks = 0; ks < C::RS; ++ks) {
-        const bf16x8 ot = lds_b128(dOTs + (32 * ct + l32) * C::STRT + 16 * ks + 8 * hh);
-        dv[ct] = mfma32(ot, pk[ks], dv[ct]);
-        const bf16x8 qt = lds_b128(QTs + (32 * ct + l32) * C::STRT + 16 * ks + 8 * hh);
-        dk[ct] = mfma32(qt, dsk[ks], dk[ct]);
+        for (int h = 0; h < 2; ++h) {
+          dv[ct] = mfma32(ota[ct][h], pk[h], dv[ct]);
+          dk[ct] = mfma32(qta[ct][h], dsk[h], dk[ct]);
+        }
       }
     }
   };
@@ -357,16 +384,20 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdParams p) {
   int rb = rb_begin;
   if (rb < n_rb && !kept(rb)) rb = next_kept(rb);
   if (rb < n_rb) {
-    load_rb(rb);
-    store_rb(0);
+    issue(rb, 0);
+    wait_vmcnt<0>();
+    store_stats(0);
     __syncthreads();
     int buf = 0;
     while (rb < n_rb) {
       const int rn = next_kept(rb);
-      if (rn < n_rb) load_rb(rn);
+      if (rn < n_rb) issue(rn, buf ^ 1);
       compute(rb, buf);
-      if (rn < n_rb) store_rb(buf ^ 1);
-      __syncthreads();   // next block staged; this block's buffers free
+      if (rn < n_rb) {
+        wait_vmcnt<0>();
+        store_stats(buf ^ 1);
+      }
+      __syncthreads();   // next block landed; this block's buffers free
       buf ^= 1;
       rb = rn;
     }

@@ -10,6 +10,9 @@
 // recompute from the saved statistics) and accumulates dQ on chip. Nothing is
 // exchanged between workgroups, and dQ is bitwise reproducible.
 //
+// Tiles reach LDS exactly as in the forward kernel: direct global->LDS loads
+// into the swizzled layout of fa_common.hpp, three tiles in flight.
+//
 // Per wave (32 query rows) and K/V tile (BN keys):
 //   S^T  = K_tile Q_w^T        MFMA 32x32x16: K rows from LDS, Q^T in VGPRs;
 //   dP^T = V_tile dO_w^T       likewise. Each lane holds one query row, so the
@@ -28,24 +31,21 @@ namespace {
 
 template <int D>
 struct DqCfg {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;           // query rows per workgroup
   static constexpr int BN = 64;                   // keys per K/V tile
-  // K is read by 16-byte row reads (S^T) and by transposing reads (dQ^T):
-  // a stride of 12 (mod 64) dwords serves both without 2-way conflicts on the
-  // row reads; V is read by row reads only.
-  static constexpr int STRK = D + 24;             // 152 / 88
-  static constexpr int STRV = D + 8;              // 136 / 72
+  static constexpr int C = D / 8;                 // 16-byte chunks per tile row
   static constexpr int KS = D / 16;
   static constexpr int NT = BN / 32;
   static constexpr int CT = D / 32;
-  static constexpr int CHUNKS = BN * D / 8;
-  static constexpr int CPT = CHUNKS / THREADS;
-  static constexpr int KTILE = BN * STRK;
-  static constexpr int VTILE = BN * STRV;
-  static constexpr int STAGE = KTILE + VTILE;
-  static_assert(CHUNKS % THREADS == 0, "tile must split evenly over threads");
+  static constexpr int TILE = BN * D;             // elements per K or V tile (swizzled, unpadded)
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int NSTAGE = 3;
+  static constexpr int SLOTS = BN * C / 64;
+  static constexpr int SPW = SLOTS / WAVES;
+  static constexpr int LPT = 2 * SPW;
+  static_assert(SLOTS % WAVES == 0, "tile slots split evenly over waves");
 };
 
 struct DqParams {
@@ -67,10 +67,10 @@ struct DqParams {
 };
 
 template <int D, bool CAUSAL, bool BLOCK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_bwd_dq_kernel(DqParams p) {
   using C = DqCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];  // [buffer][K tile, V tile]
+  __shared__ __attribute__((aligned(16))) bf16 smem[C::NSTAGE * C::STAGE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,9 +94,34 @@ void fa_bwd_dq_kernel(DqParams p) {
 
   int kt_end = (N + C::BN - 1) / C::BN;
   if (CAUSAL) kt_end = min(kt_end, (row0 + C::BM - 1) / C::BN + 1);
-  const uint8_t* mrow = nullptr;
-  if (BLOCK) mrow = p.blocks + bh * p.blocks_bh_stride + (int64_t)(row0 / 128) * p.nb;
-  auto kept = [&](int kt) -> bool { return !BLOCK || mrow[(kt * C::BN) / 128] != 0; };
+
+  // Block mask: the workgroup's rows span two 128-row mask rows; their bits go
+  // to LDS once. A tile is loaded if either row keeps it; a wave skips tiles
+  // its own row drops.
+  __shared__ uint32_t mbits[BLOCK ? 2 * kMaskWords : 1];
+  const int mr0 = row0 / 128;
+  const int my_mr = wrow0 / 128 - mr0;
+  if (BLOCK) {
+    const int nw = (p.nb + 63) / 64;
+    const uint8_t* grid = p.blocks + bh * p.blocks_bh_stride;
+    for (int j = wave; j < 2 * nw; j += C::WAVES) {
+      const int rr = j / nw;
+      const int b = (j % nw) * 64 + lane;
+      const bool keep = mr0 + rr < p.nb && b < p.nb && grid[(int64_t)(mr0 + rr) * p.nb + b] != 0;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+      if (lane == 0) {
+        mbits[rr * kMaskWords + 2 * (j % nw)] = (uint32_t)bal;
+        mbits[rr * kMaskWords + 2 * (j % nw) + 1] = (uint32_t)(bal >> 32);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  auto mbit = [&](int rr, int kt) -> bool {
+    const int b = (kt * C::BN) / 128;
+    return (mbits[rr * kMaskWords + (b >> 5)] >> (b & 31)) & 1u;
+  };
+  auto kept = [&](int kt) -> bool { return !BLOCK || mbit(0, kt) || mbit(1, kt); };
   auto next_kept = [&](int kt) -> int {
     ++kt;
     while (kt < kt_end && !kept(kt)) ++kt;
@@ -120,40 +145,43 @@ void fa_bwd_dq_kernel(DqParams p) {
     }
   }
 
-  u32x4 kst[C::CPT], vst[C::CPT];
-  auto load_tile = [&](int kt) {
+  // Direct global->LDS loads of one K/V tile into a stage (keys past N clamped).
+  auto issue = [&](int kt, int stage) {
+    bf16* Ks = smem + stage * C::STAGE;
+    bf16* Vs = Ks + C::TILE;
+    const int key0 = kt * C::BN;
 #pragma unroll
-    for (int c = 0; c < C::CPT; ++c) {
-      const int id = tid + c * C::THREADS;
-      const int r = id / (D / 8);
-      const int col = (id % (D / 8)) * 8;
-      const int key = min(kt * C::BN + r, N - 1);  // keys past N are masked
-      kst[c] = *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + col);
-      vst[c] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + col);
+    for (int i = 0; i < C::SPW; ++i) {
+      const int slot = wave + i * C::WAVES;
+      dma_slot<C::C>(Ks, slot, lane,
+                     [&](int r) { return Kh + (int64_t)min(key0 + r, N - 1) * D; });
+      dma_slot<C::C>(Vs, slot, lane,
+                     [&](int r) { return Vh + (int64_t)min(key0 + r, N - 1) * D; });
     }
   };
-  auto store_tile = [&](int buf) {
-    bf16* Ks = smem + buf * C::STAGE;
-    bf16* Vs = Ks + C::KTILE;
+
+  // Lane offsets inside a tile: row reads of K and V (same layout), and the
+  // transposing reads of K; sub-tile steps add compile-time constants.
+  int roff[C::KS], toff_t[C::CT][2];
 #pragma unroll
-    for (int c = 0; c < C::CPT; ++c) {
-      const int id = tid + c * C::THREADS;
-      const int r = id / (D / 8);
-      const int col = (id % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Ks + r * C::STRK + col) = kst[c];
-      *reinterpret_cast<u32x4*>(Vs + r * C::STRV + col) = vst[c];
-    }
-  };
+  for (int kk = 0; kk < C::KS; ++kk) roff[kk] = toff<C::C>(l32, 16 * kk + 8 * hh);
+#pragma unroll
+  for (int ct = 0; ct < C::CT; ++ct) {
+    const int n0 = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
+    toff_t[ct][0] = toff<C::C>(4 * hh + (i16 >> 2), n0);
+    toff_t[ct][1] = toff<C::C>(8 + 4 * hh + (i16 >> 2), n0);
+  }
 
   f32x16 acc[C::CT];
 #pragma unroll
   for (int ct = 0; ct < C::CT; ++ct) acc[ct] = f32x16{};
 
-  auto compute = [&](int kt, int buf) {
-    const bf16* Ks = smem + buf * C::STAGE;
-    const bf16* Vs = Ks + C::KTILE;
+  auto compute = [&](int kt, int stage) {
+    const bf16* Ks = smem + stage * C::STAGE;
+    const bf16* Vs = Ks + C::TILE;
     const int kbase = kt * C::BN;
     if (CAUSAL && kbase > wrow0 + 31) return;   // this wave's rows see none of the tile
+    if (BLOCK && !mbit(my_mr, kt)) return;     // nor of a tile its mask row drops
 
     f32x16 s[C::NT], dp[C::NT];
 #pragma unroll
@@ -165,9 +193,9 @@ void fa_bwd_dq_kernel(DqParams p) {
     for (int kk = 0; kk < C::KS; ++kk) {
 #pragma unroll
       for (int st = 0; st < C::NT; ++st) {
-        const bf16x8 a = lds_b128(Ks + (32 * st + l32) * C::STRK + 16 * kk + 8 * hh);
+        const bf16x8 a = lds_b128(Ks + roff[kk] + 32 * st * D);
         s[st] = mfma32(a, qf[kk], s[st]);
-        const bf16x8 b = lds_b128(Vs + (32 * st + l32) * C::STRV + 16 * kk + 8 * hh);
+        const bf16x8 b = lds_b128(Vs + roff[kk] + 32 * st * D);
         dp[st] = mfma32(b, gf[kk], dp[st]);
       }
     }
@@ -193,33 +221,35 @@ void fa_bwd_dq_kernel(DqParams p) {
     // order (lane half hh: keys 4hh..4hh+3 and 8+4hh..8+4hh+3 of each 16).
 #pragma unroll
     for (int ct = 0; ct < C::CT; ++ct) {
-      const int n0 = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
 #pragma unroll
       for (int ks = 0; ks < 2 * C::NT; ++ks) {
-        const int r0 = 16 * ks + 4 * hh + (i16 >> 2);
-        const i16x4 lo = lds_tr(Ks + r0 * C::STRK + n0);
-        const i16x4 hi = lds_tr(Ks + (r0 + 8) * C::STRK + n0);
+        const i16x4 lo = lds_tr(Ks + toff_t[ct][0] + 16 * ks * D);
+        const i16x4 hi = lds_tr(Ks + toff_t[ct][1] + 16 * ks * D);
         acc[ct] = mfma32(cat(lo, hi), dsk[ks], acc[ct]);
       }
     }
   };
 
+  // Three-stage ring, as in the forward kernel.
   int kt = 0;
   if (BLOCK && kt < kt_end && !kept(kt)) kt = next_kept(kt);
-  if (kt < kt_end) {
-    load_tile(kt);
-    store_tile(0);
+  int kn = kt < kt_end ? next_kept(kt) : kt_end;
+  if (kt < kt_end) issue(kt, 0);
+  wait_vmcnt<0>();   // the row operands above complete before the loop
+  if (kn < kt_end) issue(kn, 1);
+  int stage = 0;
+  while (kt < kt_end) {
+    const int knn = kn < kt_end ? next_kept(kn) : kt_end;
+    if (kn < kt_end)
+      wait_vmcnt<C::LPT>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
-    int buf = 0;
-    while (kt < kt_end) {
-      const int kn = next_kept(kt);
-      if (kn < kt_end) load_tile(kn);
-      compute(kt, buf);
-      if (kn < kt_end) store_tile(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-      kt = kn;
-    }
+    if (knn < kt_end) issue(knn, stage == 0 ? 2 : stage - 1);
+    compute(kt, stage);
+    stage = stage == 2 ? 0 : stage + 1;
+    kt = kn;
+    kn = knn;
   }
 
   // acc[ct][v] = dQ[qrow][32*ct + 8*(v/4) + 4*hh + v%4] / scale.
