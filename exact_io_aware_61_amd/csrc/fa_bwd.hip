@@ -28,6 +28,8 @@
 //   dS = P o (dP - D_i)
 //   dV_w^T += dO^T P, dK_w^T += Q^T dS    P, dS straight from registers as the
 //                                 B operand, dO^T/Q^T by 16-byte LDS reads
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -300,7 +302,10 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  auto compute = [&](int rb, int buf) {
+  // EDGE: the block has pairs to mask (causal diagonal, keys past N); interior
+  // blocks are compiled without any masking code.
+  auto compute = [&](int rb, int buf, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const bf16* Qs = tiles + buf * C::STAGE;
     const bf16* dOs = Qs + C::TILE;
     const bf16* QTs = dOs + C::TILE;
@@ -309,7 +314,6 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const float* Ds = rowstat[buf][1];
     const int row0 = rb * C::BM;
 
-    const bool edge = (CAUSAL && row0 < wkey0 + 31) || (key0 + C::BN > N);
     // One 32-row sub-tile at a time (S, dP, softmax, then its share of dV/dK):
     // the same LDS reads as a whole-block pass, with half the live registers.
 #pragma unroll
@@ -353,7 +357,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         for (int r = 0; r < 4; ++r) {
           const int v = 4 * g + r;
           float pe = fast_exp2(__builtin_fmaf(s[v], p.sl2, -l4[r]));
-          if (edge) {
+          if (EDGE) {
             const int row = row0 + rl + r;
             if ((CAUSAL && mykey > row) || mykey >= N) pe = 0.f;
           }
@@ -381,6 +385,25 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
+  // One step: stage the next kept row block, compute this one, publish.
+  auto step = [&](int& rb, int& buf, auto edge_tag) {
+    const int rn = next_kept(rb);
+    if (rn < n_rb) issue(rn, buf ^ 1);
+    compute(rb, buf, edge_tag);
+    if (rn < n_rb) {
+      wait_vmcnt<0>();
+      store_stats(buf ^ 1);
+    }
+    __syncthreads();   // next block landed; this block's buffers free
+    buf ^= 1;
+    rb = rn;
+  };
+  // Blocks that need masking come first (the causal diagonal: rows below
+  // key0 + BN - 1) or are all of them (the last key block when N is ragged);
+  // the rest run a copy of the body without any masking code.
+  auto edge_block = [&](int rb) {
+    return (CAUSAL && rb * C::BM < key0 + C::BN - 1) || key0 + C::BN > N;
+  };
   int rb = rb_begin;
   if (rb < n_rb && !kept(rb)) rb = next_kept(rb);
   if (rb < n_rb) {
@@ -389,18 +412,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     store_stats(0);
     __syncthreads();
     int buf = 0;
-    while (rb < n_rb) {
-      const int rn = next_kept(rb);
-      if (rn < n_rb) issue(rn, buf ^ 1);
-      compute(rb, buf);
-      if (rn < n_rb) {
-        wait_vmcnt<0>();
-        store_stats(buf ^ 1);
-      }
-      __syncthreads();   // next block landed; this block's buffers free
-      buf ^= 1;
-      rb = rn;
-    }
+    while (rb < n_rb && edge_block(rb)) step(rb, buf, std::true_type{});
+    while (rb < n_rb) step(rb, buf, std::false_type{});
   }
 
   // dK^T / dV^T accumulators: lane holds key mykey, columns 32*ct + 8*g + 4*hh + r.
