@@ -11,7 +11,7 @@
 // exchanged between workgroups, and dQ is bitwise reproducible.
 //
 // Tiles reach LDS exactly as in the forward kernel: direct global->LDS loads
-// into the swizzled layout of fa_common.hpp, three tiles in flight.
+// into the swizzled layout of fa_common.hpp, up to three tiles in flight.
 //
 // Per wave (32 query rows) and K/V tile (BN keys):
 //   S^T  = K_tile Q_w^T        MFMA 32x32x16: K rows from LDS, Q^T in VGPRs;
@@ -29,9 +29,11 @@
 namespace fa {
 namespace {
 
-template <int D>
+template <int D, bool BLOCK>
 struct DqCfg {
-  static constexpr int WAVES = 8;
+  // A block mask works on 128-row blocks: masked launches use 128-row
+  // workgroups so that every wave of a workgroup keeps the same tiles.
+  static constexpr int WAVES = BLOCK ? 4 : 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;           // query rows per workgroup
   static constexpr int BN = 64;                   // keys per K/V tile
@@ -41,10 +43,11 @@ struct DqCfg {
   static constexpr int CT = D / 32;
   static constexpr int TILE = BN * D;             // elements per K or V tile (swizzled, unpadded)
   static constexpr int STAGE = 2 * TILE;
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = (BLOCK && D == 128) ? 2 : 3;
   static constexpr int SLOTS = BN * C / 64;
   static constexpr int SPW = SLOTS / WAVES;
   static constexpr int LPT = 2 * SPW;
+  static constexpr int NMR = BM / 128;            // block-mask rows per workgroup
   static_assert(SLOTS % WAVES == 0, "tile slots split evenly over waves");
 };
 
@@ -67,9 +70,9 @@ struct DqParams {
 };
 
 template <int D, bool CAUSAL, bool BLOCK>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__((DqCfg<D, BLOCK>::THREADS)) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_bwd_dq_kernel(DqParams p) {
-  using C = DqCfg<D>;
+  using C = DqCfg<D, BLOCK>;
   __shared__ __attribute__((aligned(16))) bf16 smem[C::NSTAGE * C::STAGE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
@@ -98,13 +101,13 @@ void fa_bwd_dq_kernel(DqParams p) {
   // Block mask: the workgroup's rows span two 128-row mask rows; their bits go
   // to LDS once. A tile is loaded if either row keeps it; a wave skips tiles
   // its own row drops.
-  __shared__ uint32_t mbits[BLOCK ? 2 * kMaskWords : 1];
+  __shared__ uint32_t mbits[BLOCK ? C::NMR * kMaskWords : 1];
   const int mr0 = row0 / 128;
   const int my_mr = wrow0 / 128 - mr0;
   if (BLOCK) {
     const int nw = (p.nb + 63) / 64;
     const uint8_t* grid = p.blocks + bh * p.blocks_bh_stride;
-    for (int j = wave; j < 2 * nw; j += C::WAVES) {
+    for (int j = wave; j < C::NMR * nw; j += C::WAVES) {
       const int rr = j / nw;
       const int b = (j % nw) * 64 + lane;
       const bool keep = mr0 + rr < p.nb && b < p.nb && grid[(int64_t)(mr0 + rr) * p.nb + b] != 0;
@@ -121,7 +124,7 @@ void fa_bwd_dq_kernel(DqParams p) {
     const int b = (kt * C::BN) / 128;
     return (mbits[rr * kMaskWords + (b >> 5)] >> (b & 31)) & 1u;
   };
-  auto kept = [&](int kt) -> bool { return !BLOCK || mbit(0, kt) || mbit(1, kt); };
+  auto kept = [&](int kt) -> bool { return !BLOCK || mbit(0, kt) || (C::NMR > 1 && mbit(1, kt)); };
   auto next_kept = [&](int kt) -> int {
     ++kt;
     while (kt < kt_end && !kept(kt)) ++kt;
@@ -230,24 +233,30 @@ void fa_bwd_dq_kernel(DqParams p) {
     }
   };
 
-  // Three-stage ring, as in the forward kernel.
+  // Ring of NSTAGE stages, as in the forward kernel.
   int kt = 0;
   if (BLOCK && kt < kt_end && !kept(kt)) kt = next_kept(kt);
   int kn = kt < kt_end ? next_kept(kt) : kt_end;
   if (kt < kt_end) issue(kt, 0);
-  wait_vmcnt<0>();   // the row operands above complete before the loop
-  if (kn < kt_end) issue(kn, 1);
+  // The row operand loads above must be complete before the loop: a wait for
+  // them inside the loop would also wait for the tiles in flight.
+  wait_vmcnt<0>();
+  if (C::NSTAGE == 3 && kn < kt_end) issue(kn, 1);
   int stage = 0;
   while (kt < kt_end) {
     const int knn = kn < kt_end ? next_kept(kn) : kt_end;
-    if (kn < kt_end)
+    if (C::NSTAGE == 3 && kn < kt_end)
       wait_vmcnt<C::LPT>();
     else
       wait_vmcnt<0>();
     __syncthreads();
-    if (knn < kt_end) issue(knn, stage == 0 ? 2 : stage - 1);
+    if (C::NSTAGE == 3) {
+      if (knn < kt_end) issue(knn, stage == 0 ? 2 : stage - 1);
+    } else {
+      if (kn < kt_end) issue(kn, stage ^ 1);
+    }
     compute(kt, stage);
-    stage = stage == 2 ? 0 : stage + 1;
+    stage = stage == C::NSTAGE - 1 ? 0 : stage + 1;
     kt = kn;
     kn = knn;
   }
@@ -268,9 +277,9 @@ void fa_bwd_dq_kernel(DqParams p) {
   }
 }
 
-template <int D>
-hipError_t launch_dq_d(const BwdArgs& a, hipStream_t stream) {
-  using C = DqCfg<D>;
+template <int D, bool CAUSAL, bool BLOCK>
+hipError_t launch_one(const BwdArgs& a, hipStream_t stream) {
+  using C = DqCfg<D, BLOCK>;
   DqParams p;
   p.q = static_cast<const bf16*>(a.q);
   p.k = static_cast<const bf16*>(a.k);
@@ -288,20 +297,16 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t stream) {
   p.blocks_bh_stride = a.mask.bh_stride;
   p.nb = a.mask.nb;
   const dim3 grid((unsigned)p.n_row_blocks * (unsigned)a.BH);
-  const dim3 block(C::THREADS);
-  const bool blk = a.mask.blocks != nullptr;
-  if (a.mask.causal) {
-    if (blk)
-      hipLaunchKernelGGL((fa_bwd_dq_kernel<D, true, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((fa_bwd_dq_kernel<D, true, false>), grid, block, 0, stream, p);
-  } else {
-    if (blk)
-      hipLaunchKernelGGL((fa_bwd_dq_kernel<D, false, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((fa_bwd_dq_kernel<D, false, false>), grid, block, 0, stream, p);
-  }
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL, BLOCK>), grid, dim3(C::THREADS), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dq_d(const BwdArgs& a, hipStream_t stream) {
+  const bool blk = a.mask.blocks != nullptr;
+  if (a.mask.causal)
+    return blk ? launch_one<D, true, true>(a, stream) : launch_one<D, true, false>(a, stream);
+  return blk ? launch_one<D, false, true>(a, stream) : launch_one<D, false, false>(a, stream);
 }
 
 }  // namespace

@@ -7,8 +7,8 @@
 // workgroup talks to another. Inside the workgroup every wave owns 32 query
 // rows (the "split-Q" partition of the same overview): K/V tiles are shared
 // through LDS, and no partial results are exchanged between waves. Tiles reach
-// LDS by direct global->LDS loads (no staging registers), three tiles in
-// flight, in the swizzled layout of fa_common.hpp.
+// LDS by direct global->LDS loads (no staging registers), up to three tiles
+// in flight, in the swizzled layout of fa_common.hpp.
 //
 // Per wave and K/V tile (BN keys):
 //   S^T = K_tile Q_wave^T       MFMA 32x32x16, K read from LDS, Q^T held in VGPRs.
@@ -38,9 +38,11 @@
 namespace fa {
 namespace {
 
-template <int D>
+template <int D, bool BLOCK>
 struct FwdCfg {
-  static constexpr int WAVES = 8;
+  // A block mask works on 128-row blocks: masked launches use 128-row
+  // workgroups so that every wave of a workgroup keeps the same tiles.
+  static constexpr int WAVES = BLOCK ? 4 : 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;           // query rows per workgroup
   static constexpr int BN = 64;                   // keys per K/V tile
@@ -50,10 +52,13 @@ struct FwdCfg {
   static constexpr int CT = D / 32;               // 32-column sub-tiles of O^T
   static constexpr int TILE = BN * D;             // elements per K or V tile (swizzled, unpadded)
   static constexpr int STAGE = 2 * TILE;          // K tile, V tile
-  static constexpr int NSTAGE = 3;                // tiles in flight: two loading, one in use
+  // Tiles in flight (three: two loading while one is used; two where LDS
+  // must hold two workgroups per CU).
+  static constexpr int NSTAGE = (BLOCK && D == 128) ? 2 : 3;
   static constexpr int SLOTS = BN * C / 64;       // 1 KiB direct-load slots per tile
   static constexpr int SPW = SLOTS / WAVES;       // ... per wave
   static constexpr int LPT = 2 * SPW;             // direct loads per thread per K+V tile
+  static constexpr int NMR = BM / 128;            // block-mask rows per workgroup
   static_assert(SLOTS % WAVES == 0, "tile slots split evenly over waves");
 };
 
@@ -77,9 +82,9 @@ struct FwdParams {
 };
 
 template <int D, bool CAUSAL, bool BLOCK>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__((FwdCfg<D, BLOCK>::THREADS)) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_kernel(FwdParams p) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, BLOCK>;
   __shared__ __attribute__((aligned(16))) bf16 smem[C::NSTAGE * C::STAGE];  // [stage][K, V]
 
   const int tid = threadIdx.x;
@@ -110,13 +115,13 @@ void fa_fwd_kernel(FwdParams p) {
   // Block mask: the workgroup's rows span two 128-row mask rows; their bits go
   // to LDS once (so the tile loop reads no global memory besides the tiles). A
   // tile is loaded if either row keeps it; a wave skips tiles its row drops.
-  __shared__ uint32_t mbits[BLOCK ? 2 * kMaskWords : 1];
+  __shared__ uint32_t mbits[BLOCK ? C::NMR * kMaskWords : 1];
   const int mr0 = row0 / 128;
   const int my_mr = wrow0 / 128 - mr0;   // this wave's mask row: 0 or 1
   if (BLOCK) {
     const int nw = (p.nb + 63) / 64;
     const uint8_t* grid = p.blocks + bh * p.blocks_bh_stride;
-    for (int j = wave; j < 2 * nw; j += C::WAVES) {
+    for (int j = wave; j < C::NMR * nw; j += C::WAVES) {
       const int rr = j / nw;
       const int b = (j % nw) * 64 + lane;
       const bool keep = mr0 + rr < p.nb && b < p.nb && grid[(int64_t)(mr0 + rr) * p.nb + b] != 0;
@@ -133,7 +138,7 @@ void fa_fwd_kernel(FwdParams p) {
     const int b = (kt * C::BN) / 128;
     return (mbits[rr * kMaskWords + (b >> 5)] >> (b & 31)) & 1u;
   };
-  auto kept = [&](int kt) -> bool { return !BLOCK || mbit(0, kt) || mbit(1, kt); };
+  auto kept = [&](int kt) -> bool { return !BLOCK || mbit(0, kt) || (C::NMR > 1 && mbit(1, kt)); };
   auto next_kept = [&](int kt) -> int {
     ++kt;
     while (kt < kt_end && !kept(kt)) ++kt;
@@ -274,29 +279,33 @@ void fa_fwd_kernel(FwdParams p) {
     }
   };
 
-  // Three-stage ring: while tile i is computed, tiles i+1 and i+2 are loading.
-  // At the top of each step a thread waits for its own loads of tile i, the
-  // barrier then publishes every thread's loads and guarantees that no wave
-  // still reads the stage the load of tile i+2 overwrites.
+  // Ring of NSTAGE stages: while tile i is computed, tiles i+1 (and i+2 with
+  // three stages) are loading. At the top of each step a thread waits for its
+  // own loads of tile i; the barrier then publishes every thread's loads and
+  // guarantees that no wave still reads the stage the next load overwrites.
   int kt = 0;
   if (BLOCK && kt < kt_end && !kept(kt)) kt = next_kept(kt);
   int kn = kt < kt_end ? next_kept(kt) : kt_end;
   if (kt < kt_end) issue(kt, 0);
-  // The Q operand loads above must be complete before the loop: a wait for
+  // The row operand loads above must be complete before the loop: a wait for
   // them inside the loop would also wait for the tiles in flight.
   wait_vmcnt<0>();
-  if (kn < kt_end) issue(kn, 1);
+  if (C::NSTAGE == 3 && kn < kt_end) issue(kn, 1);
   int stage = 0;
   while (kt < kt_end) {
     const int knn = kn < kt_end ? next_kept(kn) : kt_end;
-    if (kn < kt_end)
+    if (C::NSTAGE == 3 && kn < kt_end)
       wait_vmcnt<C::LPT>();
     else
       wait_vmcnt<0>();
     __syncthreads();
-    if (knn < kt_end) issue(knn, stage == 0 ? 2 : stage - 1);
+    if (C::NSTAGE == 3) {
+      if (knn < kt_end) issue(knn, stage == 0 ? 2 : stage - 1);
+    } else {
+      if (kn < kt_end) issue(kn, stage ^ 1);
+    }
     compute(kt, stage);
-    stage = stage == 2 ? 0 : stage + 1;
+    stage = stage == C::NSTAGE - 1 ? 0 : stage + 1;
     kt = kn;
     kn = knn;
   }
@@ -322,9 +331,9 @@ void fa_fwd_kernel(FwdParams p) {
   }
 }
 
-template <int D>
-hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-  using C = FwdCfg<D>;
+template <int D, bool CAUSAL, bool BLOCK>
+hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
+  using C = FwdCfg<D, BLOCK>;
   FwdParams p;
   p.q = static_cast<const bf16*>(a.q);
   p.k = static_cast<const bf16*>(a.k);
@@ -339,20 +348,16 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   p.blocks_bh_stride = a.mask.bh_stride;
   p.nb = a.mask.nb;
   const dim3 grid((unsigned)p.n_row_blocks * (unsigned)a.BH);
-  const dim3 block(C::THREADS);
-  const bool blk = a.mask.blocks != nullptr;
-  if (a.mask.causal) {
-    if (blk)
-      hipLaunchKernelGGL((fa_fwd_kernel<D, true, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((fa_fwd_kernel<D, true, false>), grid, block, 0, stream, p);
-  } else {
-    if (blk)
-      hipLaunchKernelGGL((fa_fwd_kernel<D, false, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((fa_fwd_kernel<D, false, false>), grid, block, 0, stream, p);
-  }
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, BLOCK>), grid, dim3(C::THREADS), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
+  const bool blk = a.mask.blocks != nullptr;
+  if (a.mask.causal)
+    return blk ? launch_one<D, true, true>(a, stream) : launch_one<D, true, false>(a, stream);
+  return blk ? launch_one<D, false, true>(a, stream) : launch_one<D, false, false>(a, stream);
 }
 
 }  // namespace
