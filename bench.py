@@ -39,7 +39,8 @@ METRIC = "attention fwd & fwd+bwd TFLOP/s and % of bf16 MFMA peak, N=2k–32k"
 # MI355X dense bf16 MFMA peak: 256 CU x 4096 FLOP/clk/CU x 2.4 GHz.
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ("fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_common.hpp", "fa_kernels.hpp")
+KERNEL_SOURCES = ("fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_common.hpp",
+                  "fa_kernels.hpp")
 
 
 def parse():
@@ -183,14 +184,14 @@ def main():
         check(lib.fa_fwd(P(qg), P(kg), P(vg), P(o), P(lse), B, H, N, d, sc, mask, sp))
 
     def pre():
-        check(lib.fa_bwd_preprocess(P(qg), P(o), P(dog), B, H, N, d, P(ws), wsn, sp))
+        check(lib.fa_bwd_preprocess(P(o), P(dog), P(lse), B, H, N, d, P(ws), wsn, sp))
 
     def dkdv():
-        check(lib.fa_bwd_dkdv(P(qg), P(kg), P(vg), P(dog), P(lse), P(dk), P(dv), B, H, N, d, sc,
+        check(lib.fa_bwd_dkdv(P(qg), P(kg), P(vg), P(dog), P(dk), P(dv), B, H, N, d, sc,
                               mask, P(ws), wsn, sp))
 
     def dqk():
-        check(lib.fa_bwd_dq(P(qg), P(kg), P(vg), P(dog), P(lse), P(dq), B, H, N, d, sc, mask,
+        check(lib.fa_bwd_dq(P(qg), P(kg), P(vg), P(dog), P(dq), B, H, N, d, sc, mask,
                             P(ws), wsn, sp))
 
     stages = [("fa_fwd_kernel", fwd), ("fa_bwd_pre_kernel", pre),

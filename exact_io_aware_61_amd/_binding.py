@@ -52,9 +52,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp,
                            sz, vp]
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, sz, vp]
-    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz,
-                                vp]
-    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz, vp]
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz, vp]
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz, vp]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.fa_strerror.argtypes = [ctypes.c_int]
@@ -158,26 +157,26 @@ def backward(q, k, v, o, lse, do, *, causal: bool = False, block_mask=None,
     return dq, dk, dv
 
 
-def bwd_preprocess(q, o, do, ws):
-    B, H, N, d = _shape(q, o, do)
-    _check(load().fa_bwd_preprocess(_ptr(q), _ptr(o), _ptr(do), B, H, N, d, _ptr(ws), ws.numel(),
-                                    _stream(o)))
+def bwd_preprocess(o, do, lse, ws):
+    B, H, N, d = _shape(o, do)
+    _check(load().fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(lse), B, H, N, d, _ptr(ws),
+                                    ws.numel(), _stream(o)))
 
 
-def bwd_dkdv(q, k, v, do, lse, dk, dv, ws, *, causal=False, block_mask=None, scale=None):
+def bwd_dkdv(q, k, v, do, dk, dv, ws, *, causal=False, block_mask=None, scale=None):
     B, H, N, d = _shape(q, k, v, do)
     scale = default_scale(d) if scale is None else float(scale)
     mptr, keep = _mask(causal, block_mask, B, H, N, q.device)
-    _check(load().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv),
+    _check(load().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
                               B, H, N, d, scale, mptr, _ptr(ws), ws.numel(), _stream(q)))
     del keep
 
 
-def bwd_dq(q, k, v, do, lse, dq, ws, *, causal=False, block_mask=None, scale=None):
+def bwd_dq(q, k, v, do, dq, ws, *, causal=False, block_mask=None, scale=None):
     B, H, N, d = _shape(q, k, v, do)
     scale = default_scale(d) if scale is None else float(scale)
     mptr, keep = _mask(causal, block_mask, B, H, N, q.device)
-    _check(load().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dq),
+    _check(load().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq),
                             B, H, N, d, scale, mptr, _ptr(ws), ws.numel(), _stream(q)))
     del keep
 

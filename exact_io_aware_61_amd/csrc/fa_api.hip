@@ -77,15 +77,14 @@ int padded_rows(int N) {
   return (N + r - 1) / r * r;
 }
 
-// Workspace layout, each part starting on a 256-byte boundary:
-//   D_i      float32 [BH * N]
-//   Q^T      bf16    [BH * d * Np]   Np = N rounded up to the row padding
-//   dO^T     bf16    [BH * d * Np]
-size_t ws_part_d(const Shape& s) { return round256((size_t)s.bh() * s.N * sizeof(float)); }
-size_t ws_part_t(const Shape& s) {
-  return round256((size_t)s.bh() * s.d * padded_rows(s.N) * 2);
+// Workspace layout, each part starting on a 256-byte boundary
+// (Np = N rounded up to the row padding):
+//   D_i             float32 [BH][Np]
+//   LSE_i log2(e)   float32 [BH][Np]
+size_t ws_part(const Shape& s) {
+  return round256((size_t)s.bh() * padded_rows(s.N) * sizeof(float));
 }
-size_t workspace_bytes(const Shape& s) { return ws_part_d(s) + 2 * ws_part_t(s); }
+size_t workspace_bytes(const Shape& s) { return 2 * ws_part(s); }
 
 int check_workspace(const void* ws, size_t bytes, const Shape& s) {
   if (ws == nullptr) return FA_ERR_WORKSPACE;
@@ -97,9 +96,7 @@ int check_workspace(const void* ws, size_t bytes, const Shape& s) {
 void split_workspace(void* ws, const Shape& s, fa::BwdArgs* a) {
   char* base = static_cast<char*>(ws);
   a->dvec = reinterpret_cast<float*>(base);
-  base += ws_part_d(s);
-  a->qt = base;
-  a->dot = base + ws_part_t(s);
+  a->l2 = reinterpret_cast<float*>(base + ws_part(s));
   a->Np = padded_rows(s.N);
 }
 
@@ -114,7 +111,7 @@ int launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 // Checks shared by the two gradient stages (dK/dV and dQ); outs are the stage's
 // bf16 outputs (n_out of them). On success fills *a; *empty reports a zero extent.
 int check_grad_stage(const void* q, const void* k, const void* v, const void* dout,
-                     const float* lse, void* const* outs, int n_out, int B, int H, int N, int d,
+                     void* const* outs, int n_out, int B, int H, int N, int d,
                      float scale, const fa_mask_t* mask, void* workspace, size_t ws_bytes,
                      fa::BwdArgs* a, bool* empty) {
   const Shape s{B, H, N, d};
@@ -124,27 +121,24 @@ int check_grad_stage(const void* q, const void* k, const void* v, const void* do
   FA_TRY(check_mask(mask, s, &m));
   *empty = s.empty();
   if (*empty) return FA_OK;
-  if (!q || !k || !v || !dout || !lse) return FA_ERR_NULL;
+  if (!q || !k || !v || !dout) return FA_ERR_NULL;
   for (int i = 0; i < n_out; ++i)
     if (!outs[i]) return FA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned4(lse))
-    return FA_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout)) return FA_ERR_ALIGN;
   for (int i = 0; i < n_out; ++i)
     if (!aligned16(outs[i])) return FA_ERR_ALIGN;
   FA_TRY(check_workspace(workspace, ws_bytes, s));
   const int64_t tb = s.elems() * 2;
-  const Range ins[6] = {range(q, tb), range(k, tb), range(v, tb), range(dout, tb),
-                        range(lse, s.bh() * N * 4),
+  const Range ins[5] = {range(q, tb), range(k, tb), range(v, tb), range(dout, tb),
                         range(workspace, (int64_t)workspace_bytes(s))};
   Range out_r[2];
   for (int i = 0; i < n_out; ++i) out_r[i] = range(outs[i], tb);
-  if (any_overlap(out_r, n_out, ins, 6)) return FA_ERR_ALIAS;
+  if (any_overlap(out_r, n_out, ins, 5)) return FA_ERR_ALIAS;
   *a = fa::BwdArgs{};
   a->q = q;
   a->k = k;
   a->v = v;
   a->dout = dout;
-  a->lse = lse;
   a->BH = (int)s.bh();
   a->N = N;
   a->d = d;
@@ -200,22 +194,22 @@ int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes) {
   return FA_OK;
 }
 
-int fa_bwd_preprocess(const void* q, const void* o, const void* dout, int B, int H, int N, int d,
-                      void* workspace, size_t ws_bytes, void* stream) {
+int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int N,
+                      int d, void* workspace, size_t ws_bytes, void* stream) {
   const Shape s{B, H, N, d};
   FA_TRY(check_shape(s));
   if (s.empty()) return FA_OK;
-  if (!q || !o || !dout) return FA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(o) || !aligned16(dout)) return FA_ERR_ALIGN;
+  if (!o || !dout || !lse) return FA_ERR_NULL;
+  if (!aligned16(o) || !aligned16(dout) || !aligned4(lse)) return FA_ERR_ALIGN;
   FA_TRY(check_workspace(workspace, ws_bytes, s));
   const int64_t tb = s.elems() * 2;
-  const Range ins[3] = {range(q, tb), range(o, tb), range(dout, tb)};
+  const Range ins[3] = {range(o, tb), range(dout, tb), range(lse, s.bh() * N * 4)};
   const Range outs[1] = {range(workspace, (int64_t)workspace_bytes(s))};
   if (any_overlap(outs, 1, ins, 3)) return FA_ERR_ALIAS;
   fa::BwdArgs a{};
-  a.q = q;
   a.o = o;
   a.dout = dout;
+  a.lse = lse;
   a.BH = (int)s.bh();
   a.N = N;
   a.d = d;
@@ -223,13 +217,12 @@ int fa_bwd_preprocess(const void* q, const void* o, const void* dout, int B, int
   return launched(fa::launch_bwd_preprocess(a, static_cast<hipStream_t>(stream)));
 }
 
-int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                void* dk, void* dv, int B, int H, int N, int d, float scale,
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, int B, int H, int N, int d, float scale,
                 const fa_mask_t* mask, void* workspace, size_t ws_bytes, void* stream) {
   void* const outs[2] = {dk, dv};
   fa::BwdArgs a;
   bool empty = false;
-  FA_TRY(check_grad_stage(q, k, v, dout, lse, outs, 2, B, H, N, d, scale, mask, workspace,
+  FA_TRY(check_grad_stage(q, k, v, dout, outs, 2, B, H, N, d, scale, mask, workspace,
                           ws_bytes, &a, &empty));
   if (empty) return FA_OK;
   a.dk = dk;
@@ -237,13 +230,12 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, c
   return launched(fa::launch_bwd_dkdv(a, static_cast<hipStream_t>(stream)));
 }
 
-int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-              void* dq, int B, int H, int N, int d, float scale, const fa_mask_t* mask,
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B, int H, int N, int d, float scale, const fa_mask_t* mask,
               void* workspace, size_t ws_bytes, void* stream) {
   void* const outs[1] = {dq};
   fa::BwdArgs a;
   bool empty = false;
-  FA_TRY(check_grad_stage(q, k, v, dout, lse, outs, 1, B, H, N, d, scale, mask, workspace,
+  FA_TRY(check_grad_stage(q, k, v, dout, outs, 1, B, H, N, d, scale, mask, workspace,
                           ws_bytes, &a, &empty));
   if (empty) return FA_OK;
   a.dq = dq;
@@ -270,10 +262,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   const Range outs[4] = {range(dq, tb), range(dk, tb), range(dv, tb),
                          range(workspace, (int64_t)workspace_bytes(s))};
   if (any_overlap(outs, 4, ins, 6)) return FA_ERR_ALIAS;
-  FA_TRY(fa_bwd_preprocess(q, o, dout, B, H, N, d, workspace, ws_bytes, stream));
-  FA_TRY(fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, H, N, d, scale, mask, workspace, ws_bytes,
-                     stream));
-  return fa_bwd_dq(q, k, v, dout, lse, dq, B, H, N, d, scale, mask, workspace, ws_bytes, stream);
+  FA_TRY(fa_bwd_preprocess(o, dout, lse, B, H, N, d, workspace, ws_bytes, stream));
+  FA_TRY(fa_bwd_dkdv(q, k, v, dout, dk, dv, B, H, N, d, scale, mask, workspace, ws_bytes, stream));
+  return fa_bwd_dq(q, k, v, dout, dq, B, H, N, d, scale, mask, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -17,7 +17,9 @@
 //   S^T  = K_tile Q_w^T        MFMA 32x32x16: K rows from LDS, Q^T in VGPRs;
 //   dP^T = V_tile dO_w^T       likewise. Each lane holds one query row, so the
 //                              row's LSE and D_i = dO_i . O_i are lane scalars.
-//   P  = 2^(S scale log2e - LSE_i log2e)      (masked pairs -> 0)
+//   P  = 2^(S scale log2e - L2_i)    L2_i = LSE_i log2e from the preprocess
+//                                    (+inf for rows that see no key); masked
+//                                    pairs -> 0
 //   dS = P o (dP - D_i)
 //   dQ^T += K_tile^T dS^T      dS^T straight from registers as the B operand
 //                              (keys in the accumulator's order), K^T by the
@@ -56,11 +58,12 @@ struct DqParams {
   const bf16* k;
   const bf16* v;
   const bf16* dout;
-  const float* lse;
-  const float* dvec;
+  const float* l2;     // [BH][Np]
+  const float* dvec;   // [BH][Np]
   bf16* dq;
   int BH;
   int N;
+  int Np;
   int n_row_blocks;
   float sl2;    // scale * log2(e)
   float scale;
@@ -141,10 +144,9 @@ void fa_bwd_dq_kernel(DqParams p) {
       qf[kk] = *reinterpret_cast<const bf16x8*>(p.q + head + (int64_t)r * D + 16 * kk + 8 * hh);
       gf[kk] = *reinterpret_cast<const bf16x8*>(p.dout + head + (int64_t)r * D + 16 * kk + 8 * hh);
     }
-    const float lse = p.lse[(int64_t)bh * N + r];
-    if (qrow < N && lse != -INFINITY) {
-      lrow = lse * kLog2e;
-      drow = p.dvec[(int64_t)bh * N + r];
+    if (qrow < N) {
+      lrow = p.l2[(int64_t)bh * p.Np + r];
+      drow = p.dvec[(int64_t)bh * p.Np + r];
     }
   }
 
@@ -285,11 +287,12 @@ hipError_t launch_one(const BwdArgs& a, hipStream_t stream) {
   p.k = static_cast<const bf16*>(a.k);
   p.v = static_cast<const bf16*>(a.v);
   p.dout = static_cast<const bf16*>(a.dout);
-  p.lse = a.lse;
+  p.l2 = a.l2;
   p.dvec = a.dvec;
   p.dq = static_cast<bf16*>(a.dq);
   p.BH = a.BH;
   p.N = a.N;
+  p.Np = a.Np;
   p.n_row_blocks = (a.N + C::BM - 1) / C::BM;
   p.sl2 = a.scale * kLog2e;
   p.scale = a.scale;

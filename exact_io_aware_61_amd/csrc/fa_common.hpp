@@ -114,6 +114,17 @@ __device__ __forceinline__ void dma16(const void* src, const bf16* lds_dst) {
                : "memory", "m0");
 }
 
+// Direct global->LDS load of 4 bytes per lane (global_load_lds_dword): lane l
+// writes LDS bytes [lds + 4 l, lds + 4 l + 4). Same ordering rules as dma16.
+__device__ __forceinline__ void dma4(const void* src, const void* lds_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds_dst));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+
 // One 1 KiB slot of a swizzled tile: lane l fills chunk position 64*slot + l,
 // fetching the chunk of the source row that the swizzle stores there.
 // row_ptr(r) returns the global address of tile row r.

@@ -38,13 +38,12 @@ struct BwdArgs {
   int BH, N, d;
   float scale;
   MaskArgs mask;
-  float* dvec;   // workspace: D_i [BH * N]
-  void* qt;      // workspace: Q^T, bf16 [BH][d][Np], rows permuted within 16-row groups
-  void* dot;     // workspace: dO^T, same layout
+  float* dvec;   // workspace: D_i = dO_i . O_i, [BH][Np] (0 past N)
+  float* l2;     // workspace: LSE_i log2(e), [BH][Np] (+inf past N and for empty rows)
   int Np;        // N rounded up to bwd_row_padding()
 };
 
-// Row padding of the transposed copies in the backward workspace.
+// Row padding of the per-row arrays in the backward workspace.
 int bwd_row_padding();
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

@@ -95,9 +95,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace fa_bwd needs, written to *bytes (pure host
- * arithmetic). The workspace holds, each part 256-byte aligned: the row terms
- * D_i = dO_i . O_i ([B, H, N] float32) and transposed bf16 copies of Q and dO
- * ([B, H, d, Np] each, Np = N rounded up to a multiple of 128).
+ * arithmetic). The workspace holds two per-row float32 arrays [B, H, Np]
+ * (Np = N rounded up to a multiple of 128), each 256-byte aligned: the row
+ * terms D_i = dO_i . O_i and LSE_i log2(e) (+inf for rows past N and rows that
+ * see no key). That is about 8 bytes per query row.
  */
 int fa_bwd_workspace_size(int B, int H, int N, int d, size_t* bytes);
 
@@ -126,20 +127,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * separately; calling them in order on one stream, with one workspace, equals
  * fa_bwd (dkdv and dq only read the workspace, so they may also run
  * concurrently once fa_bwd_preprocess has finished).
- *   fa_bwd_preprocess : D_i = sum_c dO_ic O_ic and the transposed copies of Q
- *                       and dO, into the workspace.
- *   fa_bwd_dkdv       : dK, dV (bf16).
- *   fa_bwd_dq         : dQ (bf16).
- * Argument meanings and checks are those of fa_bwd.
+ *   fa_bwd_preprocess : D_i = sum_c dO_ic O_ic and LSE_i log2(e), from o, dout
+ *                       and lse, into the workspace.
+ *   fa_bwd_dkdv       : dK, dV (bf16), from q, k, v, dout and the workspace.
+ *   fa_bwd_dq         : dQ (bf16), from q, k, v, dout and the workspace.
+ * Argument meanings and checks are those of fa_bwd; the two gradient stages
+ * take the row statistics from the workspace only, so scale and mask must be
+ * those the gradients are wanted for (the preprocess needs neither).
  */
-int fa_bwd_preprocess(const void* q, const void* o, const void* dout, int B, int H, int N, int d,
-                      void* workspace, size_t workspace_bytes, void* stream);
-int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                const float* lse, void* dk, void* dv,
+int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int N,
+                      int d, void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
                 int B, int H, int N, int d, float scale, const fa_mask_t* mask,
                 void* workspace, size_t workspace_bytes, void* stream);
-int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-              const float* lse, void* dq,
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
               int B, int H, int N, int d, float scale, const fa_mask_t* mask,
               void* workspace, size_t workspace_bytes, void* stream);
 

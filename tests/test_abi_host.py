@@ -57,7 +57,7 @@ def test_workspace_size_arithmetic(lib):
         assert lib.fa_bwd_workspace_size(B, H, N, d, ctypes.byref(n)) == OK
         r256 = lambda x: (x + 255) // 256 * 256
         Np = (N + 127) // 128 * 128
-        assert n.value == r256(B * H * N * 4) + 2 * r256(B * H * d * Np * 2)
+        assert n.value == 2 * r256(B * H * Np * 4)   # D_i and LSE_i log2(e), per padded row
     assert lib.fa_bwd_workspace_size(1, 1, 1, 96, ctypes.byref(n)) == SHAPE
     assert lib.fa_bwd_workspace_size(-1, 1, 1, 64, ctypes.byref(n)) == SHAPE
     assert lib.fa_bwd_workspace_size(1, 1, 1, 64, None) == NULL
@@ -120,19 +120,23 @@ def test_bwd_rejects_bad_arguments(lib):
     assert bwd(ws_bytes=need - 1) == WS
     assert bwd(ws_ptr=ctypes.c_void_p(0x90004)) == ALIGN
     assert bwd(dq=ctypes.c_void_p(0x10000 + 64)) == ALIAS   # dq overlaps q
-    assert lib.fa_bwd_preprocess(None, P[1], P[2], 1, 2, 256, 64, ws, need, STREAM) == NULL
-    assert lib.fa_bwd_preprocess(P[0], P[1], P[2], 1, 2, 256, 64, ws, need - 1, STREAM) == WS
-    assert lib.fa_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 1, 2, 256, 64, 0.125, None,
+    assert lib.fa_bwd_preprocess(None, P[4], P[8], 1, 2, 256, 64, ws, need, STREAM) == NULL
+    assert lib.fa_bwd_preprocess(P[3], P[4], None, 1, 2, 256, 64, ws, need, STREAM) == NULL
+    assert lib.fa_bwd_preprocess(P[3], P[4], P[8], 1, 2, 256, 64, ws, need - 1, STREAM) == WS
+    assert lib.fa_bwd_preprocess(P[3], P[4], P[8], 1, 2, 256, 64, P[4], need, STREAM) == ALIAS
+    assert lib.fa_bwd_dkdv(P[0], P[1], P[2], P[4], P[6], P[7], 1, 2, 256, 64, 0.125, None,
                            ws, 16, STREAM) == WS
-    assert lib.fa_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], None, P[6], 1, 2, 256, 64, 0.125, None,
+    assert lib.fa_bwd_dkdv(P[0], P[1], P[2], P[4], None, P[7], 1, 2, 256, 64, 0.125, None,
                            ws, need, STREAM) == NULL
-    assert lib.fa_bwd_dkdv(P[0], P[1], P[2], P[3], P[4], P[0], P[6], 1, 2, 256, 64, 0.125, None,
+    assert lib.fa_bwd_dkdv(P[0], P[1], P[2], P[4], P[0], P[7], 1, 2, 256, 64, 0.125, None,
                            ws, need, STREAM) == ALIAS   # dk overlaps q
-    assert lib.fa_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], 1, 2, 256, 64, 0.125, None, None,
+    assert lib.fa_bwd_dkdv(P[0], P[1], P[2], P[4], ws, P[7], 1, 2, 256, 64, 0.125, None,
+                           ws, need, STREAM) == ALIAS   # dk overlaps the workspace
+    assert lib.fa_bwd_dq(P[0], P[1], P[2], P[4], P[5], 1, 2, 256, 64, 0.125, None, None,
                          need, STREAM) == WS
-    assert lib.fa_bwd_dq(P[0], P[1], P[2], P[3], P[4], P[5], 1, 2, 256, 64, -1.0, None, ws, need,
+    assert lib.fa_bwd_dq(P[0], P[1], P[2], P[4], P[5], 1, 2, 256, 64, -1.0, None, ws, need,
                          STREAM) == SCALE
-    assert lib.fa_bwd_dq(P[0], P[1], P[2], P[3], P[4], ctypes.c_void_p(0x60008), 1, 2, 256, 64,
+    assert lib.fa_bwd_dq(P[0], P[1], P[2], P[4], ctypes.c_void_p(0x60008), 1, 2, 256, 64,
                          0.125, None, ws, need, STREAM) == ALIGN
 
 
