@@ -204,19 +204,26 @@ void fa_bwd_dq_kernel(DqParams p) {
         dp[st] = mfma32(b, gf[kk], dp[st]);
       }
     }
-    // s[st][v]: key kbase + 32*st + 8*(v/4) + 4*hh + v%4, query row qrow.
+    // s[st][v]: key kbase + 32*st + 8*(v/4) + 4*hh + v%4, query row qrow. Masked
+    // scores become -inf (one uniform branch per tile), so P and dS are 0 there.
     const bool edge = (CAUSAL && kbase + C::BN - 1 > wrow0) || (kbase + C::BN > N);
+    if (edge) {
+#pragma unroll
+      for (int st = 0; st < C::NT; ++st) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kbase + 32 * st + 8 * (v / 4) + 4 * hh + (v % 4);
+          if ((CAUSAL && key > qrow) || key >= N) s[st][v] = -INFINITY;
+        }
+      }
+    }
     bf16x8 dsk[2 * C::NT];
 #pragma unroll
     for (int st = 0; st < C::NT; ++st) {
       float ds[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float pe = fast_exp2(__builtin_fmaf(s[st][v], p.sl2, -lrow));
-        if (edge) {
-          const int key = kbase + 32 * st + 8 * (v / 4) + 4 * hh + (v % 4);
-          if ((CAUSAL && key > qrow) || key >= N) pe = 0.f;
-        }
+        const float pe = fast_exp2(__builtin_fmaf(s[st][v], p.sl2, -lrow));
         ds[v] = pe * (dp[st][v] - drow);
       }
       dsk[2 * st] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
