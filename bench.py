@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="the CPU oracle runs whole heads until this much time has passed "
                          "(at least one head; 0 = skip cpu_baseline)")
+    ap.add_argument("--block-keep", type=float, default=None,
+                    help="run the workload with a 128x128 block mask of this keep probability "
+                         "(off-diagonal blocks; the diagonal is always kept)")
+    ap.add_argument("--causal", action="store_true", help="add the causal mask to the workload")
     ap.add_argument("--probe", choices=["copy"], default=None)
     ap.add_argument("--probe-mib", type=int, default=1024)
     return ap.parse_args()
@@ -140,7 +144,7 @@ def main():
     import torch
 
     import exact_io_aware_61_amd as fa
-    from exact_io_aware_61_amd.workloads import WORKLOADS, kept_fraction, make_inputs
+    from exact_io_aware_61_amd.workloads import WORKLOADS, kept_fraction, make_inputs, variant
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (none visible)", file=sys.stderr)
@@ -151,6 +155,8 @@ def main():
 
     lib = fa.load()
     w = WORKLOADS[args.workload]
+    if args.block_keep is not None or args.causal:
+        w = variant(w, block_keep=args.block_keep, causal=True if args.causal else None)
     dev = torch.device("cuda:0")
     print(f"[bench] workload {w.name} B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} "
           f"block_keep={w.block_keep}", file=sys.stderr, flush=True)

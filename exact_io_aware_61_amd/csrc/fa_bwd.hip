@@ -152,8 +152,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int g16 = lane >> 4;
   const int i16 = lane & 15;
 
-  const int bh = blockIdx.x % p.BH;
-  const int kb = blockIdx.x / p.BH;   // key block; block 0 carries the most rows under causal
+  const WgCoord wc = wg_coord<BLOCK>(blockIdx.x, p.BH, (p.N + C::BN - 1) / C::BN);
+  const int bh = wc.bh;
+  const int kb = wc.blk;   // key block; block 0 carries the most rows under causal
   const int N = p.N;
   const int64_t head = (int64_t)bh * N * D;
   const bf16* __restrict__ Qh = p.q + head;

@@ -86,10 +86,10 @@ void fa_bwd_dq_kernel(DqParams p) {
   const int g16 = lane >> 4;
   const int i16 = lane & 15;
 
-  // Largest causal row blocks first; every block of one head on one XCD when
-  // B*H is a multiple of 8 (consecutive workgroups go to different XCDs).
-  const int bh = blockIdx.x % p.BH;
-  const int rb = p.n_row_blocks - 1 - blockIdx.x / p.BH;
+  // Largest causal row blocks first.
+  const WgCoord wc = wg_coord<BLOCK>(blockIdx.x, p.BH, p.n_row_blocks);
+  const int bh = wc.bh;
+  const int rb = p.n_row_blocks - 1 - wc.blk;
   const int N = p.N;
   const int64_t head = (int64_t)bh * N * D;
   const bf16* __restrict__ Kh = p.k + head;

@@ -150,3 +150,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 }  // namespace fa
+
+// Workgroup order. The dispatcher hands workgroups to the 8 XCDs round-robin
+// (workgroup i to XCD i mod 8) and each XCD has its own L2. Interleaved order
+// (HEAD_MAJOR false): head i mod BH, block i / BH, so block 0 of every head
+// goes first; with B*H a multiple of 8 all of one head's blocks still land on
+// one XCD. Head-major order (HEAD_MAJOR true, B*H a multiple of 8): workgroup
+// i = 8j + x takes head x + 8*(j / nblk) and block j mod nblk, so each XCD
+// works through its heads one after another and the tiles one head's blocks
+// re-read stay in that XCD's L2 while in use; it helps when the blocks of a
+// head read different tiles (a block mask) and costs the global largest-first
+// order that causal launches want. Callers map block 0 to their largest block.
+struct WgCoord {
+  int bh;
+  int blk;
+};
+template <bool HEAD_MAJOR>
+__device__ __forceinline__ WgCoord wg_coord(int i, int BH, int nblk) {
+  if (HEAD_MAJOR && (BH & 7) == 0) {
+    const int j = i >> 3;
+    return {(i & 7) + 8 * (j / nblk), j % nblk};
+  }
+  return {i % BH, i / BH};
+}

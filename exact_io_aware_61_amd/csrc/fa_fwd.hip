@@ -96,10 +96,9 @@ void fa_fwd_kernel(FwdParams p) {
   const int i16 = lane & 15;
 
   // Largest row blocks first: under a causal mask they carry the most tiles.
-  // Consecutive workgroups go to different XCDs; with B*H a multiple of 8
-  // every workgroup of one head lands on the same XCD and shares its L2.
-  const int bh = blockIdx.x % p.BH;
-  const int rb = p.n_row_blocks - 1 - blockIdx.x / p.BH;
+  const WgCoord wc = wg_coord<BLOCK>(blockIdx.x, p.BH, p.n_row_blocks);
+  const int bh = wc.bh;
+  const int rb = p.n_row_blocks - 1 - wc.blk;   // largest causal row blocks first
   const int N = p.N;
   const int64_t head = (int64_t)bh * N * D;
   const bf16* __restrict__ Qh = p.q + head;

@@ -80,6 +80,23 @@ def make_qkv(B: int, H: int, N: int, d: int, seed: int, with_do: bool = True):
     return q, k, v, do
 
 
+def variant(w: Workload, block_keep: float | None = None, causal: bool | None = None) -> Workload:
+    """The workload with another block-mask keep probability and/or the causal mask added.
+
+    Same shapes and seeds, so Q, K, V, dO are the same draws; the block mask is
+    drawn from the workload's mask generator with the new probability. The name
+    records the change, e.g. "sparse16k:keep=0.05+causal".
+    """
+    keep = w.block_keep if block_keep is None else float(block_keep)
+    cz = w.causal if causal is None else bool(causal)
+    tag = w.name
+    if keep != w.block_keep:
+        tag += f":keep={keep:g}"
+    if cz != w.causal:
+        tag += "+causal" if cz else "-causal"
+    return dataclasses.replace(w, name=tag, block_keep=keep, causal=cz)
+
+
 def make_block_mask(N: int, keep: float, seed: int, block: int = BLOCK) -> np.ndarray:
     """uint8 [nb, nb] with nb = ceil(N/block): 1 = keep. Bernoulli(keep) off the diagonal,
     diagonal kept."""

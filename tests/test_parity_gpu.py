@@ -13,7 +13,8 @@ import pytest
 import torch
 
 import exact_io_aware_61_amd as fa
-from exact_io_aware_61_amd.workloads import WORKLOADS, make_block_mask, make_inputs, make_qkv
+from exact_io_aware_61_amd.workloads import (WORKLOADS, make_block_mask, make_inputs, make_qkv,
+                                             variant)
 from tests.gpu_util import assert_parity, run_gpu, run_oracle, to64
 
 pytestmark = pytest.mark.gpu
@@ -48,6 +49,20 @@ def test_small_parity(N, kind, d):
     gpu = run_gpu(q, k, v, do, causal=causal, block_mask=bm, scale=scale)
     ref = run_oracle(q, k, v, do, causal=causal, block_mask=bm, scale=scale)
     assert_parity(gpu, ref, label=f"N={N} d={d} {kind}")
+
+
+@pytest.mark.parametrize("keep", [0.05, 0.1, 0.25, 0.5, 1.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_density_sweep(keep, causal):
+    """The densities of the block-sparse sweep, alone and combined with the causal mask."""
+    B, H, N, d = 1, 2, 1152, 64   # 9 x 9 mask blocks
+    q, k, v, do = make_qkv(B, H, N, d, seed=8100)
+    bm = make_block_mask(N, keep, seed=8200 + int(keep * 100))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    print(f"[case] density keep={keep} causal={causal}", flush=True)
+    gpu = run_gpu(q, k, v, do, causal=causal, block_mask=bm, scale=scale)
+    ref = run_oracle(q, k, v, do, causal=causal, block_mask=bm, scale=scale)
+    assert_parity(gpu, ref, label=f"keep={keep} causal={causal}")
 
 
 @pytest.mark.parametrize("N,d,B,H", [(1, 64, 1, 1), (17, 128, 2, 1), (65, 64, 1, 3),
@@ -226,3 +241,9 @@ def test_workload_causal32k_sampled():
 @pytest.mark.timeout(300)
 def test_workload_sparse16k_sampled():
     _sampled(WORKLOADS["sparse16k"], heads=[(0, 0), (3, 15)])
+
+
+@pytest.mark.timeout(300)
+def test_workload_sparse16k_sparsest_causal_sampled():
+    """The sparsest density of the sweep, combined with the causal mask, at full size."""
+    _sampled(variant(WORKLOADS["sparse16k"], block_keep=0.05, causal=True), heads=[(2, 9)])
