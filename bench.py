@@ -17,6 +17,9 @@ peak of MI355X. `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample
 (whole heads, forward + backward) on this host's cores, with the same FLOP
 numerator per head.
 
+--kernel softmax times the standalone row softmax (fa_softmax_rows) on a
+float32 matrix (--softmax-shape ROWSxCOLS) instead, in GB/s against HBM.
+
 --probe copy runs an elementwise kernel that reads and writes a buffer of known
 size, used to calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters.
 """
@@ -39,8 +42,8 @@ METRIC = "attention fwd & fwd+bwd TFLOP/s and % of bf16 MFMA peak, N=2k–32k"
 # MI355X dense bf16 MFMA peak: 256 CU x 4096 FLOP/clk/CU x 2.4 GHz.
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ("fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_common.hpp",
-                  "fa_kernels.hpp")
+KERNEL_SOURCES = ("fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_softmax.hip",
+                  "fa_common.hpp", "fa_kernels.hpp")
 
 
 def parse():
@@ -57,6 +60,11 @@ def parse():
                     help="run the workload with a 128x128 block mask of this keep probability "
                          "(off-diagonal blocks; the diagonal is always kept)")
     ap.add_argument("--causal", action="store_true", help="add the causal mask to the workload")
+    ap.add_argument("--kernel", choices=["attention", "softmax"], default="attention",
+                    help="attention: the fwd+bwd step (default); softmax: the standalone row "
+                         "softmax (fa_softmax_rows) on --softmax-shape")
+    ap.add_argument("--softmax-shape", default="65536x4096",
+                    help="ROWSxCOLS of the float32 matrix for --kernel softmax")
     ap.add_argument("--probe", choices=["copy"], default=None)
     ap.add_argument("--probe-mib", type=int, default=1024)
     return ap.parse_args()
@@ -131,6 +139,85 @@ def cpu_baseline(w, q, k, v, do, bm, seconds: float):
             "host_cpus": os.cpu_count()}
 
 
+def bench_softmax(args):
+    """Row softmax: one step = one fa_softmax_rows over a [rows, cols] float32 matrix.
+
+    Algorithmic traffic is one read and one write of the matrix (8 bytes per
+    element); `value` is that over the measured time, against the HBM peak.
+    """
+    import numpy as np
+    import torch
+
+    import exact_io_aware_61_amd as fa
+    rows, cols = (int(v) for v in args.softmax_shape.lower().split("x"))
+    print(f"[bench] softmax rows={rows} cols={cols}", file=sys.stderr, flush=True)
+    g = torch.Generator(device="cpu").manual_seed(4242)
+    x_cpu = torch.randn((rows, cols), generator=g, dtype=torch.float32) * 4.0
+    x = x_cpu.cuda()
+    y = torch.empty_like(x)
+    lib = fa.load()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def step():
+        rc = lib.fa_softmax_rows(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                 rows, cols, sp)
+        if rc != 0:
+            raise fa.FaError(rc, fa.strerror(rc))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(K):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(K)]))
+    nbytes = 8.0 * rows * cols
+    achieved = nbytes / (per_ms * 1e-3) / 1e9
+    value = nbytes / (wall / K) / 1e9
+    kname = "softmax_rows_reg" if (cols % 4 == 0 and cols <= 4096) else "softmax_rows_stream"
+    digest = source_digest()
+    rec = traffic_record(kname, f"{rows}x{cols}", digest)
+    result = {
+        "metric": "row softmax GB/s (one read + one write per element)", "value": round(value, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"softmax_rows {rows}x{cols}", "rows": rows, "cols": cols},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if rec is None else rec["bytes_per_launch"],
+                     "avg_launch_ms": round(per_ms, 4), "bytes_per_launch": nbytes},
+        "src": digest,
+    }
+    if args.cpu_seconds > 0:
+        # the oracle on whole rows until the time is spent (same 8-byte numerator)
+        import threadpoolctl
+        from oracle.softmax_forms import row_softmax
+        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+        xs = x_cpu.double().numpy()
+        done, dt, chunk = 0, 0.0, max(1, min(rows, (1 << 22) // max(cols, 1)))
+        while done < rows and (done == 0 or dt < args.cpu_seconds):
+            t1 = time.perf_counter()
+            row_softmax(xs[done:done + chunk])
+            dt += time.perf_counter() - t1
+            done += min(chunk, rows - done)
+        result["cpu_baseline"] = {"value": 8.0 * done * cols / dt / 1e9, "unit": "GB/s",
+                                  "cores": int(threads), "kind": "oracle",
+                                  "sample": f"{done} of {rows} rows, fp64 NumPy, {dt:.2f} s",
+                                  "seconds": dt}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -151,6 +238,9 @@ def main():
         sys.exit(1)
     if args.probe == "copy":
         probe_copy(args.probe_mib, args.steps)
+        return
+    if args.kernel == "softmax":
+        bench_softmax(args)
         return
 
     lib = fa.load()
@@ -247,6 +337,18 @@ def main():
                 "traffic": None if rec is None else rec["bytes_per_launch"],
                 "avg_launch_ms": round(per[dom], 4), "flop_per_launch": kernel_flop[dom]}
 
+    # Forward IO accounting in bytes (per launch): the compulsory traffic (Q, K, V
+    # read and O written once, LSE written), and the tile model of the tiled
+    # forward, where every block of BR query rows re-reads the K and V tiles it
+    # attends (4*N*d*ceil(N/BR)*rho per head: the Theta(N^2 d^2 / M) term) on top
+    # of reading Q and writing O once. BR is the forward's rows per workgroup.
+    br = 128 if bm is not None else 256
+    heads = w.B * w.H
+    io = {"compulsory_fwd": heads * (8 * w.N * w.d + 4 * w.N),
+          "tile_model_fwd": heads * (4 * w.N * w.d + 4 * w.N * w.d * (-(-w.N // br)) * rho
+                                     + 4 * w.N),
+          "rows_per_workgroup_fwd": br}
+
     fwd_tf = fwd_flop / (fwd_ms * 1e-3) / 1e12
     fb_ms = fwd_ms + bwd_ms
     fb_tf = step_flop / (fb_ms * 1e-3) / 1e12
@@ -264,6 +366,7 @@ def main():
                     "frac_of_peak": round(fb_tf / PEAK_BF16_TFLOPS, 4)},
         "kernel_ms": {n: round(t, 4) for n, t in per.items()},
         "roofline": roofline,
+        "io_bytes": {k: (int(v) if k != "rows_per_workgroup_fwd" else v) for k, v in io.items()},
         "src": digest,
     }
     if args.cpu_seconds > 0:

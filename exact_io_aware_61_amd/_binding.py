@@ -20,7 +20,7 @@ FA_MASK_BLOCK = 2
 MASK_BLOCK_SIZE = 128
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess", "fa_bwd_dkdv",
-           "fa_bwd_dq", "fa_strerror")
+           "fa_bwd_dq", "fa_softmax_rows", "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -54,6 +54,7 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, sz, vp]
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz, vp]
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz, vp]
+    lib.fa_softmax_rows.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.fa_strerror.argtypes = [ctypes.c_int]
@@ -179,6 +180,22 @@ def bwd_dq(q, k, v, do, dq, ws, *, causal=False, block_mask=None, scale=None):
     _check(load().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq),
                             B, H, N, d, scale, mptr, _ptr(ws), ws.numel(), _stream(q)))
     del keep
+
+
+def softmax_rows(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Softmax over the last dimension of a contiguous float32 GPU tensor (fa_softmax_rows).
+
+    `out` may be `x` itself (in place) or a separate tensor of the same shape.
+    """
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous() or x.dim() < 1:
+        raise ValueError("softmax_rows needs a contiguous float32 GPU tensor")
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous() or y.device != x.device:
+        raise ValueError("out must be a contiguous float32 tensor shaped like x on the same GPU")
+    cols = int(x.shape[-1])
+    rows = int(x.numel() // cols) if cols else 0
+    _check(load().fa_softmax_rows(_ptr(x), _ptr(y), rows, cols, _stream(x)))
+    return y
 
 
 class _AttentionFn(torch.autograd.Function):

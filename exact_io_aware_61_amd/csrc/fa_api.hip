@@ -242,6 +242,23 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, voi
   return launched(fa::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
 }
 
+int fa_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream) {
+  if (rows < 0 || cols < 0 || rows > 0x7fffffff || cols > 0x7fffffff) return FA_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FA_OK;
+  if (rows * cols >= (int64_t(1) << 40)) return FA_ERR_SHAPE;
+  if (!x || !y) return FA_ERR_NULL;
+  if (!aligned4(x) || !aligned4(y)) return FA_ERR_ALIGN;
+  const int64_t bytes = rows * cols * 4;
+  // y == x (in place) is allowed; any other overlap is not
+  if (x != y) {
+    const Range in[1] = {range(x, bytes)};
+    const Range out[1] = {range(y, bytes)};
+    if (any_overlap(out, 1, in, 1)) return FA_ERR_ALIAS;
+  }
+  fa::SoftmaxArgs a{x, y, rows, cols};
+  return launched(fa::launch_softmax_rows(a, static_cast<hipStream_t>(stream)));
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
            float scale, const fa_mask_t* mask, void* workspace, size_t ws_bytes, void* stream) {

@@ -43,6 +43,13 @@ struct BwdArgs {
   int Np;        // N rounded up to bwd_row_padding()
 };
 
+struct SoftmaxArgs {
+  const float* x;
+  float* y;
+  int64_t rows;   // 1 .. 2^31 - 1
+  int64_t cols;   // 1 .. 2^31 - 1
+};
+
 // Row padding of the per-row arrays in the backward workspace.
 int bwd_row_padding();
 
@@ -50,5 +57,6 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_softmax_rows(const SoftmaxArgs& a, hipStream_t stream);
 
 }  // namespace fa

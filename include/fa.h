@@ -144,6 +144,25 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, voi
               int B, int H, int N, int d, float scale, const fa_mask_t* mask,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Row softmax with the online normalizer ("why attention is slow" page, section
+ * on the online normalizer, attributed there to NVIDIA, 2018): for every row r,
+ *   y[r][c] = e^(x[r][c] - m_r) / sum_c' e^(x[r][c'] - m_r),  m_r = max_c x[r][c],
+ * with m_r and the denominator found in one pass over the row (the running
+ * denominator rescaled whenever the running maximum grows) and y written in a
+ * second. Entries equal to -inf get 0; a row with no finite entry is all 0.
+ * Inputs holding NaN or +inf give unspecified results.
+ *   x : input [rows, cols] float32, row-major, DEVICE pointer, read-only
+ *   y : output [rows, cols] float32, DEVICE pointer; y == x (in place) is
+ *       allowed, any other overlap is FA_ERR_ALIAS
+ *   rows, cols : 0 .. 2^31 - 1 each, rows * cols < 2^40 (either 0: no-op
+ *                returning FA_OK); otherwise FA_ERR_SHAPE
+ * x and y must be 4-byte aligned; rows that are 16-byte aligned (cols a
+ * multiple of 4, x and y 16-byte aligned) take the vectorised kernels.
+ * Asynchronous on `stream` like every entry point.
+ */
+int fa_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* fa_strerror(int status);
 

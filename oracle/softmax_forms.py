@@ -5,6 +5,8 @@ they agree in fp64 and against hand-derived values. The main attention oracle
 uses only the three-pass form; the others exist so that the recurrences the
 tiled kernel relies on are themselves pinned.
 
+* row_softmax: the plain definition over every row of a matrix (the target of
+  the standalone row-softmax kernel).
 * three_pass: "why attention is slow" (page 2), time-complexity section -
   the safe softmax in three loops: running max, denominator scaled by the
   final max, then each probability.
@@ -45,6 +47,22 @@ def three_pass(x) -> np.ndarray:
     for i, xi in enumerate(x):        # pass 3: a_i = e^(x_i - m_N) / d_N
         a[i] = math.exp(xi - m) / d
     return a
+
+
+def row_softmax(x) -> np.ndarray:
+    """Softmax of every row of a 2-D array, in fp64: the plain definition.
+
+    Row r: e^(x_rc - m_r) / sum_c e^(x_rc - m_r) with m_r the row maximum
+    (the safe softmax of the same page). Entries equal to -inf get 0. A row
+    with no finite entry has no defined softmax; the reading taken here is an
+    all-zero row, the same convention as a query row that sees no key.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m = x.max(axis=1, keepdims=True)
+    live = np.isfinite(m)
+    e = np.where(live, np.exp(x - np.where(live, m, 0.0)), 0.0)
+    tot = e.sum(axis=1, keepdims=True)
+    return np.where(live, e / np.where(live, tot, 1.0), 0.0)
 
 
 def online_normalizer(x, block: int = 1):

@@ -34,7 +34,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
-                            "fa_bwd_dkdv", "fa_bwd_dq", "fa_strerror"])
+                            "fa_bwd_dkdv", "fa_bwd_dq", "fa_softmax_rows", "fa_strerror"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -147,3 +147,14 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)
+
+
+def test_softmax_rows_rejects_bad_arguments(lib):
+    x, y = P[0], P[1]
+    assert lib.fa_softmax_rows(x, y, -1, 8, STREAM) == SHAPE
+    assert lib.fa_softmax_rows(x, y, 8, 1 << 31, STREAM) == SHAPE
+    assert lib.fa_softmax_rows(x, y, 1 << 20, 1 << 20, STREAM) == SHAPE   # rows * cols >= 2^40
+    assert lib.fa_softmax_rows(None, y, 4, 8, STREAM) == NULL
+    assert lib.fa_softmax_rows(x, ctypes.c_void_p(0x20002), 4, 8, STREAM) == ALIGN
+    assert lib.fa_softmax_rows(x, ctypes.c_void_p(0x10010), 4, 8, STREAM) == ALIAS   # overlaps x
+    assert lib.fa_softmax_rows(None, None, 0, 8, STREAM) == OK                      # empty: no-op

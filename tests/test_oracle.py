@@ -162,6 +162,34 @@ def test_p2_softmax_forms_agree(block):
                                 rel=1e-14)
 
 
+def test_row_softmax_pins():
+    """The row-softmax oracle against the pinned forms, closed forms and its conventions."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((6, 37)) * 5.0
+    x[1, [0, 5, 36]] = -np.inf
+    x[4, :] = -np.inf                      # no finite entry: all zeros (reading)
+    y = sf.row_softmax(x)
+    for r in range(x.shape[0]):
+        if r == 4:
+            assert np.all(y[r] == 0.0)
+            continue
+        np.testing.assert_allclose(y[r], sf.three_pass(x[r]), rtol=1e-13, atol=1e-300)
+        np.testing.assert_allclose(y[r], sf.two_pass(x[r], block=5), rtol=1e-13, atol=1e-300)
+        assert y[r].sum() == pytest.approx(1.0, abs=1e-13)
+    assert np.all(y[1, [0, 5, 36]] == 0.0)
+    # closed forms: a constant row is uniform; [0, ln 2] -> [1/3, 2/3]; a -inf entry is 0
+    np.testing.assert_allclose(sf.row_softmax(np.full((1, 9), 3.7)), np.full((1, 9), 1 / 9),
+                               rtol=1e-15)
+    np.testing.assert_allclose(sf.row_softmax([[0.0, math.log(2.0)]]), [[1 / 3, 2 / 3]],
+                               rtol=1e-15)
+    np.testing.assert_allclose(sf.row_softmax([[5.0, 5.0 + math.log(3.0), -np.inf]]),
+                               [[0.25, 0.75, 0.0]], rtol=1e-15)
+    # shift invariance per row, and a huge spread does not overflow
+    np.testing.assert_allclose(sf.row_softmax(x[:4] + 1000.0), y[:4], rtol=1e-12, atol=1e-300)
+    big = sf.row_softmax([[1000.0, 0.0, -1000.0]])
+    assert big[0, 0] == pytest.approx(1.0) and np.all(np.isfinite(big))
+
+
 def test_p2_online_matches_attention_row():
     """The one-pass recurrence over key blocks gives the oracle's O row and LSE."""
     rng = np.random.default_rng(8)
