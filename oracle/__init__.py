@@ -9,6 +9,7 @@ Modules:
   attention      - the materialised definition (S, P in fp64), forward and backward
   softmax_forms  - three-pass, online-normalizer and one-pass softmax recurrences
   brute          - pure-Python loops for tiny inputs (pins the NumPy version)
+  decode         - decoding: the newest Nq queries over Nk cached keys (bottom-right causal)
 """
 from .attention import (allowed, attention, attention_dq_rows, attention_head,
                         attention_rows, softmax_rows)
