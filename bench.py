@@ -20,6 +20,9 @@ numerator per head.
 --kernel softmax times the standalone row softmax (fa_softmax_rows) on a
 float32 matrix (--softmax-shape ROWSxCOLS) instead, in GB/s against HBM.
 
+--kernel decode times decoding against a KV cache (fa_decode) on
+--decode-shape BxHxNqxNkxd, in GB/s of the K/V stream against HBM.
+
 --probe copy runs an elementwise kernel that reads and writes a buffer of known
 size, used to calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters.
 """
@@ -43,7 +46,7 @@ METRIC = "attention fwd & fwd+bwd TFLOP/s and % of bf16 MFMA peak, N=2k–32k"
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_softmax.hip",
-                  "fa_common.hpp", "fa_kernels.hpp")
+                  "fa_decode.hip", "fa_common.hpp", "fa_kernels.hpp")
 
 
 def parse():
@@ -60,9 +63,14 @@ def parse():
                     help="run the workload with a 128x128 block mask of this keep probability "
                          "(off-diagonal blocks; the diagonal is always kept)")
     ap.add_argument("--causal", action="store_true", help="add the causal mask to the workload")
-    ap.add_argument("--kernel", choices=["attention", "softmax"], default="attention",
+    ap.add_argument("--kernel", choices=["attention", "softmax", "decode"], default="attention",
                     help="attention: the fwd+bwd step (default); softmax: the standalone row "
-                         "softmax (fa_softmax_rows) on --softmax-shape")
+                         "softmax (fa_softmax_rows) on --softmax-shape; decode: the newest "
+                         "queries against a KV cache (fa_decode) on --decode-shape")
+    ap.add_argument("--decode-shape", default="4x32x16x32768x128",
+                    help="BxHxNqxNkxd for --kernel decode (causal unless --decode-full)")
+    ap.add_argument("--decode-full", action="store_true",
+                    help="--kernel decode without the causal mask")
     ap.add_argument("--softmax-shape", default="65536x4096",
                     help="ROWSxCOLS of the float32 matrix for --kernel softmax")
     ap.add_argument("--probe", choices=["copy"], default=None)
@@ -218,6 +226,96 @@ def bench_softmax(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_decode(args):
+    """Decoding: one step = one fa_decode of Nq new queries against an Nk-key cache.
+
+    Algorithmic traffic: K and V read once, Q read and O, LSE written once; the
+    kernels' per-chunk partial results in the workspace are not counted.
+    """
+    import numpy as np
+    import torch
+
+    import exact_io_aware_61_amd as fa
+    from exact_io_aware_61_amd.workloads import make_qkv
+    B, H, Nq, Nk, d = (int(v) for v in args.decode_shape.lower().split("x"))
+    causal = not args.decode_full
+    print(f"[bench] decode B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal}", file=sys.stderr,
+          flush=True)
+    q, _, _, _ = make_qkv(B, H, Nq, d, 4321, with_do=False)
+    _, k, v, _ = make_qkv(B, H, Nk, d, 4322, with_do=False)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    scale = float(np.float32(1 / np.sqrt(d)))
+    o = torch.empty_like(qg)
+    lse = torch.empty((B, H, Nq), device=qg.device, dtype=torch.float32)
+    lib = fa.load()
+    n = ctypes.c_size_t()
+    lib.fa_decode_workspace_size(B, H, Nq, Nk, d, ctypes.byref(n))
+    ws = torch.empty(max(n.value, 16), device=qg.device, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def step():
+        rc = lib.fa_decode(P(qg), P(kg), P(vg), P(o), P(lse), B, H, Nq, Nk, d, scale,
+                           1 if causal else 0, P(ws), ws.numel(), sp)
+        if rc != 0:
+            raise fa.FaError(rc, fa.strerror(rc))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(K):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(K)]))
+    nbytes = float(B * H * (4 * Nk * d + 4 * Nq * d + 4 * Nq))
+    achieved = nbytes / (per_ms * 1e-3) / 1e9
+    digest = source_digest()
+    shape = f"{B}x{H}x{Nq}x{Nk}x{d}"
+    rec = traffic_record("fa_decode_split_kernel", shape, digest)
+    result = {
+        "metric": "decode GB/s (K, V, Q read and O, LSE written once)",
+        "value": round(nbytes / (wall / K) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(wall / K * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decode {shape}{' causal' if causal else ''}", "B": B, "H": H,
+                   "Nq": Nq, "Nk": Nk, "d": d, "causal": causal},
+        "roofline": {"bound": "hbm", "kernel": "fa_decode_split_kernel + fa_decode_combine_kernel",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if rec is None else rec["bytes_per_launch"],
+                     "avg_launch_ms": round(per_ms, 4), "bytes_per_launch": nbytes},
+        "src": digest,
+    }
+    if args.cpu_seconds > 0:
+        import threadpoolctl
+        from oracle.decode import decode_head
+        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+        done, dt = 0, 0.0
+        while done < B * H and (done == 0 or dt < args.cpu_seconds):
+            b, h = divmod(done, H)
+            qa, ka, va = (t[b, h].double().numpy() for t in (q, k, v))
+            t1 = time.perf_counter()
+            decode_head(qa, ka, va, scale=scale, causal=causal)
+            dt += time.perf_counter() - t1
+            done += 1
+        per_head = 4 * Nk * d + 4 * Nq * d + 4 * Nq
+        result["cpu_baseline"] = {"value": per_head * done / dt / 1e9, "unit": "GB/s",
+                                  "cores": int(threads), "kind": "oracle",
+                                  "sample": f"{done} of {B * H} heads, fp64 NumPy, {dt:.2f} s",
+                                  "seconds": dt}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -241,6 +339,9 @@ def main():
         return
     if args.kernel == "softmax":
         bench_softmax(args)
+        return
+    if args.kernel == "decode":
+        bench_decode(args)
         return
 
     lib = fa.load()

@@ -10,15 +10,16 @@ device memory. This package is the thin Python binding:
     dq, dk, dv = backward(q, k, v, o, lse, do, causal=True)
     o = attention(q, k, v, causal=True)      # torch.autograd-aware
     y = softmax_rows(x)                      # row softmax, online normalizer
+    o, lse = decode(q_new, k_cache, v_cache, causal=True)   # newest queries vs a KV cache
 
 Build the library first: python -m exact_io_aware_61_amd.build
 """
 from ._binding import (EXPORTS, FA_MASK_BLOCK, FA_MASK_CAUSAL, LIB_PATH, MASK_BLOCK_SIZE, FaError,
-                       attention, backward, bwd_dkdv, bwd_dq, bwd_preprocess,
+                       attention, backward, bwd_dkdv, bwd_dq, bwd_preprocess, decode,
                        bwd_workspace_size, default_scale, forward, load, softmax_rows, strerror,
                        workspace)
 
 __all__ = ["EXPORTS", "FA_MASK_BLOCK", "FA_MASK_CAUSAL", "LIB_PATH", "MASK_BLOCK_SIZE", "FaError",
-           "attention", "backward", "bwd_dkdv", "bwd_dq", "bwd_preprocess",
+           "attention", "backward", "bwd_dkdv", "bwd_dq", "bwd_preprocess", "decode",
            "bwd_workspace_size", "default_scale", "forward", "load", "softmax_rows", "strerror",
            "workspace"]

@@ -20,7 +20,7 @@ FA_MASK_BLOCK = 2
 MASK_BLOCK_SIZE = 128
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess", "fa_bwd_dkdv",
-           "fa_bwd_dq", "fa_softmax_rows", "fa_strerror")
+           "fa_bwd_dq", "fa_decode_workspace_size", "fa_decode", "fa_softmax_rows", "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -55,6 +55,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz, vp]
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz, vp]
     lib.fa_softmax_rows.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
+    lib.fa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.fa_strerror.argtypes = [ctypes.c_int]
@@ -180,6 +182,28 @@ def bwd_dq(q, k, v, do, dq, ws, *, causal=False, block_mask=None, scale=None):
     _check(load().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq),
                             B, H, N, d, scale, mptr, _ptr(ws), ws.numel(), _stream(q)))
     del keep
+
+
+def decode(q, k, v, *, causal: bool = False, scale: float | None = None, ws=None):
+    """Attention of the newest Nq queries q [B, H, Nq, d] over a cache k, v [B, H, Nk, d]
+    (fa_decode). Returns (o [B, H, Nq, d] bf16, lse [B, H, Nq] float32)."""
+    for t in (q, k, v):
+        if t.dim() != 4 or t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v must be contiguous 4-D bf16 GPU tensors")
+    B, H, Nq, d = (int(x) for x in q.shape)
+    if k.shape != v.shape or tuple(k.shape[:2]) != (B, H) or int(k.shape[3]) != d:
+        raise ValueError("k and v must be [B, H, Nk, d] matching q")
+    Nk = int(k.shape[2])
+    scale = default_scale(d) if scale is None else float(scale)
+    n = ctypes.c_size_t()
+    _check(load().fa_decode_workspace_size(B, H, Nq, Nk, d, ctypes.byref(n)))
+    if ws is None:
+        ws = torch.empty(max(n.value, 16), device=q.device, dtype=torch.uint8)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+    _check(load().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, scale,
+                            1 if causal else 0, _ptr(ws), ws.numel(), _stream(q)))
+    return o, lse
 
 
 def softmax_rows(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

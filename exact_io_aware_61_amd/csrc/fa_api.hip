@@ -148,6 +148,24 @@ int check_grad_stage(const void* q, const void* k, const void* v, const void* do
   return FA_OK;
 }
 
+// Decoding: shape checks and the workspace of the key split.
+int decode_shape(int B, int H, int Nq, int Nk, int d) {
+  if (B < 0 || H < 0 || Nq < 0 || Nq > 32 || Nk < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_SHAPE;
+  if ((int64_t)B * H * ((int64_t)Nk + Nq) * d >= (int64_t(1) << 40)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+size_t decode_ws_o(int64_t BH, int Nq, int Nk, int d) {
+  int ns = 1, ch = 32;
+  fa::decode_split((int)BH, Nk, &ns, &ch);
+  return round256((size_t)BH * ns * Nq * d * sizeof(float));
+}
+size_t decode_ws_ml(int64_t BH, int Nq, int Nk) {
+  int ns = 1, ch = 32;
+  fa::decode_split((int)BH, Nk, &ns, &ch);
+  return round256((size_t)BH * ns * Nq * 2 * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -240,6 +258,50 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, voi
   if (empty) return FA_OK;
   a.dq = dq;
   return launched(fa::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, size_t* bytes) {
+  if (bytes == nullptr) return FA_ERR_NULL;
+  FA_TRY(decode_shape(B, H, Nq, Nk, d));
+  const int64_t BH = (int64_t)B * H;
+  *bytes = decode_ws_o(BH, Nq, Nk, d) + decode_ws_ml(BH, Nq, Nk);
+  return FA_OK;
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Nq, int Nk, int d, float scale, int causal, void* workspace, size_t ws_bytes,
+              void* stream) {
+  FA_TRY(decode_shape(B, H, Nq, Nk, d));
+  FA_TRY(check_scale(scale));
+  if (causal != 0 && causal != 1) return FA_ERR_MASK;
+  const int64_t BH = (int64_t)B * H;
+  if (BH == 0 || Nq == 0) return FA_OK;
+  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(o) || !aligned4(lse) || !aligned16(k) || !aligned16(v))
+    return FA_ERR_ALIGN;
+  const size_t need = decode_ws_o(BH, Nq, Nk, d) + decode_ws_ml(BH, Nq, Nk);
+  if (workspace == nullptr || ws_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  const int64_t qb = BH * Nq * d * 2, kb = BH * (int64_t)Nk * d * 2;
+  const Range ins[3] = {range(q, qb), range(k, kb), range(v, kb)};
+  const Range outs[3] = {range(o, qb), range(lse, BH * Nq * 4), range(workspace, (int64_t)need)};
+  if (any_overlap(outs, 3, ins, 3)) return FA_ERR_ALIAS;
+  fa::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = (int)BH;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  fa::decode_split(a.BH, Nk, &a.nsplit, &a.chunk);
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_ws_o(BH, Nq, Nk, d));
+  return launched(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 int fa_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream) {

@@ -50,6 +50,25 @@ struct SoftmaxArgs {
   int64_t cols;   // 1 .. 2^31 - 1
 };
 
+struct DecodeArgs {
+  const void* q;    // [BH][Nq][d]
+  const void* k;    // [BH][Nk][d]
+  const void* v;
+  void* o;          // [BH][Nq][d]
+  float* lse;       // [BH][Nq]
+  int BH, Nq, Nk, d;
+  float scale;
+  bool causal;
+  float* part_o;    // workspace: [BH][nsplit][Nq][d]
+  float* part_ml;   // workspace: [BH][nsplit][Nq][2]
+  int nsplit;       // from decode_split
+  int chunk;
+};
+
+// Key split of the decoding kernels: nsplit chunks of `chunk` keys (a multiple
+// of 32) cover Nk.
+void decode_split(int BH, int Nk, int* nsplit, int* chunk);
+
 // Row padding of the per-row arrays in the backward workspace.
 int bwd_row_padding();
 
@@ -58,5 +77,6 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_softmax_rows(const SoftmaxArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace fa

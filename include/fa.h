@@ -145,6 +145,33 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, voi
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decoding against a key/value cache. The pages name inference with a KV cache
+ * and FlashDecoding (lecture summary, remark after section 3.1, conclusion)
+ * without defining them; what is computed is attention of the Nq newest
+ * queries of each (b, h) over its Nk cached keys, query i sitting at position
+ * Nk - Nq + i:
+ *   O_i = sum_j softmax_j(scale q_i . k_j) v_j over the visible keys j,
+ *   lse_i = ln sum_j e^(scale q_i . k_j)  (natural log),
+ * where every key is visible, or with causal = 1 only keys j <= Nk - Nq + i
+ * (aligned at the bottom right; the top-left rule of fa_fwd when Nq = Nk). A
+ * query that sees no key gets O = 0 and lse = -inf. The keys are split into
+ * chunks processed in parallel, each by the tiled online softmax of fa_fwd; a
+ * second kernel merges the chunks' (max, denominator, output) states.
+ *   q      : [B, H, Nq, d] bf16        k, v : [B, H, Nk, d] bf16 (the cache)
+ *   o      : output [B, H, Nq, d] bf16  lse  : output [B, H, Nq] float32
+ *   causal : 0 or 1 (other values: FA_ERR_MASK)
+ *   workspace : DEVICE buffer of at least fa_decode_workspace_size() bytes,
+ *               caller-owned, contents irrelevant on entry, overwritten
+ * Limits: 0 <= Nq <= 32, Nk >= 0 (k and v may be NULL when Nk = 0),
+ * d in {64, 128}, B*H*(Nq+Nk)*d < 2^40. Errors and streams as above; outputs
+ * and workspace must not overlap each other or any input.
+ */
+int fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, size_t* bytes);
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Nq, int Nk, int d, float scale, int causal,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Row softmax with the online normalizer ("why attention is slow" page, section
  * on the online normalizer, attributed there to NVIDIA, 2018): for every row r,
  *   y[r][c] = e^(x[r][c] - m_r) / sum_c' e^(x[r][c'] - m_r),  m_r = max_c x[r][c],

@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
-                            "fa_bwd_dkdv", "fa_bwd_dq", "fa_softmax_rows", "fa_strerror"])
+                            "fa_bwd_dkdv", "fa_bwd_dq", "fa_decode_workspace_size", "fa_decode",
+                            "fa_softmax_rows", "fa_strerror"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -158,3 +159,29 @@ def test_softmax_rows_rejects_bad_arguments(lib):
     assert lib.fa_softmax_rows(x, ctypes.c_void_p(0x20002), 4, 8, STREAM) == ALIGN
     assert lib.fa_softmax_rows(x, ctypes.c_void_p(0x10010), 4, 8, STREAM) == ALIAS   # overlaps x
     assert lib.fa_softmax_rows(None, None, 0, 8, STREAM) == OK                      # empty: no-op
+
+
+def test_decode_rejects_bad_arguments(lib):
+    n = ctypes.c_size_t()
+    assert lib.fa_decode_workspace_size(2, 4, 16, 4096, 128, ctypes.byref(n)) == OK
+    assert n.value > 0 and n.value % 256 == 0
+    assert lib.fa_decode_workspace_size(1, 1, 16, 64, 128, ctypes.byref(n)) == OK
+    need = n.value   # placeholder buffers 64 KiB apart: keep the shapes below that size
+    assert lib.fa_decode_workspace_size(2, 4, 33, 4096, 128, ctypes.byref(n)) == SHAPE
+    assert lib.fa_decode_workspace_size(2, 4, 8, 4096, 96, ctypes.byref(n)) == SHAPE
+    ws = P[11]
+
+    def dec(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], Nq=16, Nk=64, d=128, scale=0.1,
+            causal=1, w=ws, wb=need):
+        return lib.fa_decode(q, k, v, o, lse, 1, 1, Nq, Nk, d, scale, causal, w, wb, STREAM)
+
+    assert dec(Nq=33) == SHAPE
+    assert dec(scale=float("nan")) == SCALE
+    assert dec(causal=2) == MASK
+    assert dec(q=None) == NULL
+    assert dec(k=None) == NULL
+    assert dec(o=ctypes.c_void_p(0x40008)) == ALIGN
+    assert dec(w=None) == WS
+    assert dec(wb=need - 1) == WS
+    assert dec(o=ctypes.c_void_p(0x10000 + 32)) == ALIAS          # o inside q
+    assert dec(Nq=0) == OK and dec(q=None, Nq=0) == OK              # nothing to do

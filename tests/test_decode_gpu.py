@@ -1,0 +1,87 @@
+"""GPU parity of decoding against a KV cache (fa_decode) with the fp64 oracle.
+
+Same bar as the training forward: O max-abs error <= 1e-2 and LSE max-abs
+error <= 1e-3 over all compared rows (bf16 inputs and outputs, fp32
+accumulation, P rounded to bf16 before the P V product).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_61_amd as fa
+from exact_io_aware_61_amd.workloads import make_qkv
+from oracle.decode import decode as decode_ref
+from oracle.decode import decode_head
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    fa.load()
+    torch.cuda.init()
+
+
+def _inputs(B, H, Nq, Nk, d, seed):
+    q, _, _, _ = make_qkv(B, H, Nq, d, seed, with_do=False)
+    _, k, v, _ = make_qkv(B, H, Nk, d, seed + 1, with_do=False)
+    return q, k, v
+
+
+def _compare(o, lse, ref, heads=None):
+    o = o.double().cpu().numpy()
+    lse = lse.double().cpu().numpy()
+    sel = (slice(None),) if heads is None else tuple(np.array(x) for x in zip(*heads))
+    ro, rl = ref["o"][sel], ref["lse"][sel]
+    go, gl = o[sel], lse[sel]
+    assert np.max(np.abs(go - ro)) <= 1e-2, np.max(np.abs(go - ro))
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(gl))
+    assert np.all(gl[~fin] == -np.inf) and np.all(go[~fin] == 0.0)
+    if fin.any():
+        assert np.max(np.abs(gl[fin] - rl[fin])) <= 1e-3, np.max(np.abs(gl[fin] - rl[fin]))
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d", [(1, 2, 1, 1, 64), (1, 2, 1, 37, 64), (2, 3, 4, 300, 128),
+                                         (1, 2, 16, 1000, 128), (1, 1, 32, 2049, 64),
+                                         (2, 2, 8, 5, 128), (1, 3, 3, 0, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_parity(B, H, Nq, Nk, d, causal):
+    q, k, v = _inputs(B, H, Nq, Nk, d, seed=500 + Nq * 7 + Nk)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    print(f"[case] decode B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal}", flush=True)
+    o, lse = fa.decode(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref = decode_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale=scale,
+                     causal=causal)
+    _compare(o, lse, ref)
+
+
+def test_decode_square_matches_training_forward():
+    """Nq = Nk with the causal mask is the training forward (top-left = bottom-right)."""
+    q, k, v = _inputs(1, 2, 32, 32, 128, seed=91)
+    print("[case] decode square vs fa_fwd", flush=True)
+    o, lse = fa.decode(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    o2, lse2 = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(o.float() - o2.float())).item() <= 1e-2
+    assert torch.max(torch.abs(lse - lse2)).item() <= 1e-3
+
+
+@pytest.mark.timeout(300)
+def test_decode_bench_shape_sampled():
+    """The benchmark's shape (B=4, H=32, Nq=16, Nk=32768, d=128, causal), oracle on sampled heads."""
+    B, H, Nq, Nk, d = 4, 32, 16, 32768, 128
+    q, k, v = _inputs(B, H, Nq, Nk, d, seed=4321)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    print("[case] decode 4x32x16x32768x128 sampled", flush=True)
+    o, lse = fa.decode(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    for b, h in [(0, 0), (3, 31), (2, 17)]:
+        ro, rl = decode_head(q[b, h].double().numpy(), k[b, h].double().numpy(),
+                             v[b, h].double().numpy(), scale=scale, causal=True)
+        assert np.max(np.abs(o[b, h] - ro)) <= 1e-2
+        assert np.max(np.abs(lse[b, h] - rl)) <= 1e-3
