@@ -46,7 +46,7 @@ METRIC = "attention fwd & fwd+bwd TFLOP/s and % of bf16 MFMA peak, N=2k–32k"
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_softmax.hip",
-                  "fa_decode.hip", "fa_common.hpp", "fa_kernels.hpp")
+                  "fa_decode.hip", "fa_fwd_kv_outer.hip", "fa_common.hpp", "fa_kernels.hpp")
 
 
 def parse():
@@ -63,10 +63,13 @@ def parse():
                     help="run the workload with a 128x128 block mask of this keep probability "
                          "(off-diagonal blocks; the diagonal is always kept)")
     ap.add_argument("--causal", action="store_true", help="add the causal mask to the workload")
-    ap.add_argument("--kernel", choices=["attention", "softmax", "decode"], default="attention",
+    ap.add_argument("--kernel", choices=["attention", "softmax", "decode", "fwd-kv-outer"],
+                    default="attention",
                     help="attention: the fwd+bwd step (default); softmax: the standalone row "
                          "softmax (fa_softmax_rows) on --softmax-shape; decode: the newest "
-                         "queries against a KV cache (fa_decode) on --decode-shape")
+                         "queries against a KV cache (fa_decode) on --decode-shape; "
+                         "fwd-kv-outer: the forward in the K/V-outer loop order "
+                         "(fa_fwd_kv_outer) beside fa_fwd on --workload")
     ap.add_argument("--decode-shape", default="4x32x16x32768x128",
                     help="BxHxNqxNkxd for --kernel decode (causal unless --decode-full)")
     ap.add_argument("--decode-full", action="store_true",
@@ -316,6 +319,97 @@ def bench_decode(args):
     print(json.dumps(result), flush=True)
 
 
+def kv_outer_io_model(N: int, d: int, causal: bool, heads: int) -> float:
+    """Device bytes of the K/V-outer forward per launch, counted from its loops.
+
+    Per head: K, V read once; for every visited (K/V block, Q block) pair the Q
+    block is read and O (float32), m, l are read (except at the first K/V block)
+    and written; a last sweep reads O, m, l and writes O (bf16) and LSE.
+    Blocks: 128 query rows, 64 keys.
+    """
+    BM, BN = 128, 64
+    Tr, Tc = -(-N // BM), -(-N // BN)
+    visits = sum(Tr - (j * BN // BM if causal else 0) for j in range(Tc))
+    per_visit_write = 4 * BM * d + 8 * BM
+    per_visit = 2 * BM * d + per_visit_write
+    per_head = (4 * N * d + visits * per_visit + (visits - Tr) * per_visit_write
+                + 4 * N * d + 8 * N + 2 * N * d + 4 * N)
+    return float(heads * per_head)
+
+
+def bench_kv_outer(args):
+    """The K/V-outer forward and fa_fwd on the same workload: time and device bytes."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_61_amd as fa
+    from exact_io_aware_61_amd.workloads import WORKLOADS, kept_fraction, make_inputs
+    w = WORKLOADS[args.workload]
+    if w.block_keep is not None:
+        print("fwd-kv-outer has no block mask", file=sys.stderr)
+        sys.exit(2)
+    print(f"[bench] fwd-kv-outer on {w.name}", file=sys.stderr, flush=True)
+    q, k, v, _, _ = make_inputs(w, with_do=False)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(qg)
+    lse = torch.empty((w.B, w.H, w.N), device=qg.device, dtype=torch.float32)
+    lib = fa.load()
+    n = ctypes.c_size_t()
+    lib.fa_fwd_kv_outer_workspace_size(w.B, w.H, w.N, w.d, ctypes.byref(n))
+    ws = torch.empty(max(n.value, 16), device=qg.device, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    mask = None
+    if w.causal:
+        mask_s = fa._binding.FaMask(fa.FA_MASK_CAUSAL, fa.MASK_BLOCK_SIZE, None, 0)
+        mask = ctypes.byref(mask_s)
+
+    def kvo():
+        rc = lib.fa_fwd_kv_outer(P(qg), P(kg), P(vg), P(o), P(lse), w.B, w.H, w.N, w.d, w.scale,
+                                 1 if w.causal else 0, P(ws), ws.numel(), sp)
+        if rc != 0:
+            raise fa.FaError(rc, fa.strerror(rc))
+
+    def fwd():
+        rc = lib.fa_fwd(P(qg), P(kg), P(vg), P(o), P(lse), w.B, w.H, w.N, w.d, w.scale, mask, sp)
+        if rc != 0:
+            raise fa.FaError(rc, fa.strerror(rc))
+
+    def timed(f):
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record(stream)
+        for i in range(args.steps):
+            f()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]))
+
+    t_kvo = timed(kvo)
+    t_fwd = timed(fwd)
+    rho = kept_fraction(w.N, w.causal, None)
+    flop = 4.0 * w.B * w.H * w.N * w.N * w.d * rho
+    heads = w.B * w.H
+    model_kvo = kv_outer_io_model(w.N, w.d, w.causal, heads)
+    br = 256
+    model_fwd = heads * (4 * w.N * w.d + 4 * w.N * w.d * (-(-w.N // br)) * rho + 4 * w.N)
+    result = {
+        "metric": "forward TFLOP/s, K/V-outer loop order", "value": round(flop / t_kvo / 1e9, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_kvo, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal},
+        "kv_outer_ms": round(t_kvo, 4), "fa_fwd_ms": round(t_fwd, 4),
+        "io_model_bytes": {"kv_outer": model_kvo, "fa_fwd_tile_model": model_fwd},
+        "roofline": None, "cpu_baseline": None, "src": source_digest(),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -342,6 +436,9 @@ def main():
         return
     if args.kernel == "decode":
         bench_decode(args)
+        return
+    if args.kernel == "fwd-kv-outer":
+        bench_kv_outer(args)
         return
 
     lib = fa.load()

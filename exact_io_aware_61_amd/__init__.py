@@ -16,10 +16,12 @@ Build the library first: python -m exact_io_aware_61_amd.build
 """
 from ._binding import (EXPORTS, FA_MASK_BLOCK, FA_MASK_CAUSAL, LIB_PATH, MASK_BLOCK_SIZE, FaError,
                        attention, backward, bwd_dkdv, bwd_dq, bwd_preprocess, decode,
+                       forward_kv_outer,
                        bwd_workspace_size, default_scale, forward, load, softmax_rows, strerror,
                        workspace)
 
 __all__ = ["EXPORTS", "FA_MASK_BLOCK", "FA_MASK_CAUSAL", "LIB_PATH", "MASK_BLOCK_SIZE", "FaError",
            "attention", "backward", "bwd_dkdv", "bwd_dq", "bwd_preprocess", "decode",
+           "forward_kv_outer",
            "bwd_workspace_size", "default_scale", "forward", "load", "softmax_rows", "strerror",
            "workspace"]

@@ -20,7 +20,8 @@ FA_MASK_BLOCK = 2
 MASK_BLOCK_SIZE = 128
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess", "fa_bwd_dkdv",
-           "fa_bwd_dq", "fa_decode_workspace_size", "fa_decode", "fa_softmax_rows", "fa_strerror")
+           "fa_bwd_dq", "fa_decode_workspace_size", "fa_decode", "fa_fwd_kv_outer_workspace_size",
+           "fa_fwd_kv_outer", "fa_softmax_rows", "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -57,6 +58,8 @@ def load() -> ctypes.CDLL:
     lib.fa_softmax_rows.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
     lib.fa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.fa_fwd_kv_outer_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.fa_fwd_kv_outer.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.fa_strerror.argtypes = [ctypes.c_int]
@@ -182,6 +185,20 @@ def bwd_dq(q, k, v, do, dq, ws, *, causal=False, block_mask=None, scale=None):
     _check(load().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq),
                             B, H, N, d, scale, mptr, _ptr(ws), ws.numel(), _stream(q)))
     del keep
+
+
+def forward_kv_outer(q, k, v, *, causal: bool = False, scale: float | None = None):
+    """The forward in the K/V-outer loop order (fa_fwd_kv_outer): same (o, lse) as forward()."""
+    B, H, N, d = _shape(q, k, v)
+    scale = default_scale(d) if scale is None else float(scale)
+    n = ctypes.c_size_t()
+    _check(load().fa_fwd_kv_outer_workspace_size(B, H, N, d, ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 16), device=q.device, dtype=torch.uint8)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    _check(load().fa_fwd_kv_outer(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, scale,
+                                  1 if causal else 0, _ptr(ws), ws.numel(), _stream(q)))
+    return o, lse
 
 
 def decode(q, k, v, *, causal: bool = False, scale: float | None = None, ws=None):

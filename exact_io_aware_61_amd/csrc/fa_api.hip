@@ -166,6 +166,11 @@ size_t decode_ws_ml(int64_t BH, int Nq, int Nk) {
   return round256((size_t)BH * ns * Nq * 2 * sizeof(float));
 }
 
+// Workspace of the K/V-outer forward: O float32 [BH][N][d], then m and l [BH][N].
+size_t kvo_ws_o(const Shape& s) { return round256((size_t)s.bh() * s.N * s.d * sizeof(float)); }
+size_t kvo_ws_v(const Shape& s) { return round256((size_t)s.bh() * s.N * sizeof(float)); }
+size_t kvo_workspace_bytes(const Shape& s) { return kvo_ws_o(s) + 2 * kvo_ws_v(s); }
+
 }  // namespace
 
 extern "C" {
@@ -302,6 +307,50 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_ws_o(BH, Nq, Nk, d));
   return launched(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd_kv_outer_workspace_size(int B, int H, int N, int d, size_t* bytes) {
+  if (bytes == nullptr) return FA_ERR_NULL;
+  const Shape s{B, H, N, d};
+  FA_TRY(check_shape(s));
+  *bytes = kvo_workspace_bytes(s);
+  return FA_OK;
+}
+
+int fa_fwd_kv_outer(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int N, int d, float scale, int causal, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  const Shape s{B, H, N, d};
+  FA_TRY(check_shape(s));
+  FA_TRY(check_scale(scale));
+  if (causal != 0 && causal != 1) return FA_ERR_MASK;
+  if (s.empty()) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_ALIGN;
+  if (workspace == nullptr || ws_bytes < kvo_workspace_bytes(s)) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  const int64_t tb = s.elems() * 2;
+  const Range ins[3] = {range(q, tb), range(k, tb), range(v, tb)};
+  const Range outs[3] = {range(o, tb), range(lse, s.bh() * N * 4),
+                         range(workspace, (int64_t)kvo_workspace_bytes(s))};
+  if (any_overlap(outs, 3, ins, 3)) return FA_ERR_ALIAS;
+  fa::KvOuterArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = (int)s.bh();
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  char* w = static_cast<char*>(workspace);
+  a.ow = reinterpret_cast<float*>(w);
+  a.mw = reinterpret_cast<float*>(w + kvo_ws_o(s));
+  a.lw = reinterpret_cast<float*>(w + kvo_ws_o(s) + kvo_ws_v(s));
+  return launched(fa::launch_fwd_kv_outer(a, static_cast<hipStream_t>(stream)));
 }
 
 int fa_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream) {

@@ -69,6 +69,20 @@ struct DecodeArgs {
 // of 32) cover Nk.
 void decode_split(int BH, int Nk, int* nsplit, int* chunk);
 
+struct KvOuterArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int BH, N, d;
+  float scale;
+  bool causal;
+  float* ow;   // workspace: O float32 [BH][N][d]
+  float* mw;   // workspace: m [BH][N]
+  float* lw;   // workspace: l [BH][N]
+};
+
 // Row padding of the per-row arrays in the backward workspace.
 int bwd_row_padding();
 
@@ -78,5 +92,6 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_softmax_rows(const SoftmaxArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_fwd_kv_outer(const KvOuterArgs& a, hipStream_t stream);
 
 }  // namespace fa

@@ -145,6 +145,25 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, voi
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward in the loop order of the lecture summary's algorithm overview
+ * (section 3.3; the first FlashAttention): O, l, m are kept in device memory
+ * (the workspace, float32), the outer loop walks the K/V blocks and the inner
+ * loop every Q block, reading and writing back O_i, l_i, m_i at each step with
+ * the normalised online-softmax recurrence of section 3.2; one workgroup per
+ * (b, h). Same result as fa_fwd (O bf16, lse natural log, causal = 0 or 1; no
+ * block mask); it exists to measure the IO of that order against fa_fwd's
+ * (query blocks outer, FlashAttention-2 overview), not for speed.
+ *   workspace : DEVICE buffer of at least fa_fwd_kv_outer_workspace_size()
+ *               bytes (O float32 [B, H, N, d], then m, l float32 [B, H, N],
+ *               each part 256-byte aligned), contents irrelevant on entry
+ * Arguments, limits and errors otherwise as fa_fwd.
+ */
+int fa_fwd_kv_outer_workspace_size(int B, int H, int N, int d, size_t* bytes);
+int fa_fwd_kv_outer(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decoding against a key/value cache. The pages name inference with a KV cache
  * and FlashDecoding (lecture summary, remark after section 3.1, conclusion)
  * without defining them; what is computed is attention of the Nq newest

@@ -35,6 +35,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
                             "fa_bwd_dkdv", "fa_bwd_dq", "fa_decode_workspace_size", "fa_decode",
+                            "fa_fwd_kv_outer_workspace_size", "fa_fwd_kv_outer",
                             "fa_softmax_rows", "fa_strerror"])
 
 
@@ -185,3 +186,21 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(wb=need - 1) == WS
     assert dec(o=ctypes.c_void_p(0x10000 + 32)) == ALIAS          # o inside q
     assert dec(Nq=0) == OK and dec(q=None, Nq=0) == OK              # nothing to do
+
+
+def test_kv_outer_rejects_bad_arguments(lib):
+    n = ctypes.c_size_t()
+    assert lib.fa_fwd_kv_outer_workspace_size(1, 2, 100, 64, ctypes.byref(n)) == OK
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert n.value == r256(2 * 100 * 64 * 4) + 2 * r256(2 * 100 * 4)
+    need = n.value
+
+    def kvo(q=P[0], o=P[3], causal=1, w=P[10], wb=need, d=64):
+        return lib.fa_fwd_kv_outer(q, P[1], P[2], o, P[4], 1, 2, 100, d, 0.125, causal, w, wb,
+                                   STREAM)
+
+    assert kvo(d=80) == SHAPE
+    assert kvo(causal=3) == MASK
+    assert kvo(q=None) == NULL
+    assert kvo(w=None) == WS and kvo(wb=need - 4) == WS
+    assert kvo(o=ctypes.c_void_p(0x10000 + 16)) == ALIAS
