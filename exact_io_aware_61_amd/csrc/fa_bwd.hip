@@ -20,7 +20,7 @@
 // dK/dV kernel, per workgroup of 4 waves = 128 keys; wave w owns keys
 // key0 + 32w .. +31, keeps their K and V rows in VGPRs and their dK^T, dV^T
 // accumulators on chip. Per block of BM query rows (the Q and dO tiles and the
-// rows' L2 and D reach LDS by direct global->LDS loads, three blocks ahead),
+// rows' L2 and D reach LDS by direct global->LDS loads, 2-3 blocks ahead),
 // per wave and 32-row sub-tile:
 //   S  = Q K_w^T, dP = dO V_w^T   MFMA 32x32x16, Q/dO rows by 16-byte LDS reads;
 //                                 each lane holds one key column.
@@ -256,98 +256,40 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // EDGE: the block has pairs to mask (causal diagonal, keys past N); interior
-  // blocks are compiled without any masking code.
-  auto compute = [&](int rb, int stage, auto edge_tag) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
+  // Software pipeline over 32-row sub-tiles, one wave per SIMD, so the wave's
+  // own instruction order decides what overlaps. At the start of a sub-tile
+  // its Q/dO row operands are already in registers (read during the previous
+  // sub-tile's dV/dK products); its transposed operands and row statistics
+  // are read between its S/dP products, two reads per product; after the
+  // softmax, the dV/dK products run with one read of the next sub-tile's rows
+  // after each. Scheduling-group barriers pin that interleave (left alone, the
+  // compiler pairs each read with the product that uses it, or bunches all the
+  // reads, which overfills the LDS request queue of the four waves).
+  bf16x8 qa[C::KS], ga[C::KS];
+  auto read_rows = [&](int stage, int it) {
     const bf16* Qs = smem + stage * C::STAGE;
     const bf16* dOs = Qs + C::TILE;
-    const float* Ls = reinterpret_cast<const float*>(dOs + C::TILE);
-    const float* Ds = Ls + C::BM;
-    const int row0 = rb * C::BM;
 #pragma unroll
-    for (int it = 0; it < C::IT; ++it) {
-      // All operand reads of the sub-tile's S and dP go out before its MFMAs
-      // (the scheduling barrier keeps the compiler from pairing each read with
-      // its MFMA, which would expose the LDS latency once per MFMA).
-      bf16x8 qa[C::KS], ga[C::KS];
-#pragma unroll
-      for (int kk = 0; kk < C::KS; ++kk) {
-        qa[kk] = lds_b128(Qs + qoff[kk] + 32 * it * D);
-        ga[kk] = lds_b128(dOs + qoff[kk] + 32 * it * D);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < C::KS; ++kk) {
-        s = mfma32(qa[kk], kf[kk], s);
-        dp = mfma32(ga[kk], vf[kk], dp);
-      }
-      // dV/dK operands of this sub-tile, read now and consumed after the
-      // softmax: lane gets head-dim column 32ct + l32 of the 16-row group's rows
-      // 4hh..4hh+3 and 8+4hh..8+4hh+3.
-      bf16x8 ota[C::CT][2], qta[C::CT][2];
-#pragma unroll
-      for (int ct = 0; ct < C::CT; ++ct) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int ro = (32 * it + 16 * h) * D;
-          ota[ct][h] = cat(lds_tr(dOs + troff[ct][0] + ro), lds_tr(dOs + troff[ct][1] + ro));
-          qta[ct][h] = cat(lds_tr(Qs + troff[ct][0] + ro), lds_tr(Qs + troff[ct][1] + ro));
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // s[v]: row row0 + 32*it + 8*(v/4) + 4*hh + v%4, key mykey.
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rl = 32 * it + 8 * g + 4 * hh;   // local row of v = 4g
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + rl);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + rl);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int v = 4 * g + r;
-          float pe = fast_exp2(__builtin_fmaf(s[v], p.sl2, -l4[r]));
-          if (EDGE) {
-            const int row = row0 + rl + r;
-            if ((CAUSAL && mykey > row) || mykey >= N) pe = 0.f;
-          }
-          pv[v] = pe;
-          dsv[v] = pe * (dp[v] - d4[r]);
-        }
-      }
-      bf16x8 pk[2], dsk[2];
-      pk[0] = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-      pk[1] = to_bf16x8(pv[8], pv[9], pv[10], pv[11], pv[12], pv[13], pv[14], pv[15]);
-      dsk[0] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-      dsk[1] = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
-#pragma unroll
-      for (int ct = 0; ct < C::CT; ++ct) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          dv[ct] = mfma32(ota[ct][h], pk[h], dv[ct]);
-          dk[ct] = mfma32(qta[ct][h], dsk[h], dk[ct]);
-        }
-      }
+    for (int kk = 0; kk < C::KS; ++kk) {
+      qa[kk] = lds_b128(Qs + qoff[kk] + 32 * it * D);
+      ga[kk] = lds_b128(dOs + qoff[kk] + 32 * it * D);
     }
   };
 
-  // Ring of four stages: while block j is computed, the next three kept blocks
-  // are loading. At the top of each step a thread waits for its own loads of
-  // block j (loads complete in issue order, so it waits until no more than the
-  // later blocks' loads are outstanding); the barrier then publishes every
-  // thread's loads and guarantees that no wave still reads the stage the next
-  // issue overwrites (the one block j-1 used).
-  auto wait_block = [&](int later) {   // later: blocks issued after this one (0..2)
+  // Ring of four stages. Loads run two to three blocks ahead: after the softmax
+  // of the last sub-tile of block j each thread waits for its own loads of
+  // block j+1 (loads complete in issue order, so it waits until no more than
+  // the loads of the block after that are outstanding); the barrier then
+  // publishes every thread's loads of block j+1 and guarantees that every wave
+  // has finished block j-1, whose stage the loads of block j+3 then take.
+  auto wait_block = [&](int later) {   // later: blocks issued after the awaited one (0 or 1)
     constexpr int A = 2 * C::SPW;       // loads per block, tile-only waves
     constexpr int B = 2 * C::SPW + 1;   // loads per block, row-array loaders
     if (row_loader) {
-      if (later == 2) wait_vmcnt<2 * B>();
-      else if (later == 1) wait_vmcnt<B>();
+      if (later == 1) wait_vmcnt<B>();
       else wait_vmcnt<0>();
     } else {
-      if (later == 2) wait_vmcnt<2 * A>();
-      else if (later == 1) wait_vmcnt<A>();
+      if (later == 1) wait_vmcnt<A>();
       else wait_vmcnt<0>();
     }
   };
@@ -359,25 +301,152 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   if (r1 < n_rb) issue(r1, 1);
   if (r2 < n_rb) issue(r2, 2);
   int stage = 0;
-  auto step = [&](auto edge_tag) {
-    const int r3 = r2 < n_rb ? next_kept(r2) : n_rb;
-    wait_block((r1 < n_rb ? 1 : 0) + (r2 < n_rb ? 1 : 0));
+  if (rb < n_rb) {
+    // block rb: wait until only the loads of r1 and r2 are outstanding
+    const int later = (r1 < n_rb ? 1 : 0) + (r2 < n_rb ? 1 : 0);
+    constexpr int A = 2 * C::SPW, B = 2 * C::SPW + 1;
+    if (row_loader) {
+      if (later == 2) wait_vmcnt<2 * B>();
+      else if (later == 1) wait_vmcnt<B>();
+      else wait_vmcnt<0>();
+    } else {
+      if (later == 2) wait_vmcnt<2 * A>();
+      else if (later == 1) wait_vmcnt<A>();
+      else wait_vmcnt<0>();
+    }
     __syncthreads();
-    if (r3 < n_rb) issue(r3, (stage + 3) & 3);
-    compute(rb, stage, edge_tag);
+    read_rows(0, 0);
+  }
+
+  // One row block. EDGE: the block has pairs to mask (causal diagonal, keys
+  // past N); interior blocks are compiled without any masking code.
+  auto block = [&](auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const bf16* Qs = smem + stage * C::STAGE;
+    const bf16* dOs = Qs + C::TILE;
+    const float* Ls = reinterpret_cast<const float*>(dOs + C::TILE);
+    const float* Ds = Ls + C::BM;
+    const int row0 = rb * C::BM;
+#pragma unroll
+    for (int it = 0; it < C::IT; ++it) {
+      // Region A: this sub-tile's transposed operands and row statistics are
+      // read while its S/dP products run (two reads per product).
+      bf16x8 ota[C::CT][2], qta[C::CT][2];
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int rl = 32 * it + 8 * g + 4 * hh;
+        l4[g] = *reinterpret_cast<const f32x4*>(Ls + rl);
+        d4[g] = *reinterpret_cast<const f32x4*>(Ds + rl);
+      }
+#pragma unroll
+      for (int ct = 0; ct < C::CT; ++ct) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ro = (32 * it + 16 * h) * D;
+          ota[ct][h] = cat(lds_tr(dOs + troff[ct][0] + ro), lds_tr(dOs + troff[ct][1] + ro));
+          qta[ct][h] = cat(lds_tr(Qs + troff[ct][0] + ro), lds_tr(Qs + troff[ct][1] + ro));
+        }
+      }
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < C::KS; ++kk) {
+        s = mfma32(qa[kk], kf[kk], s);
+        dp = mfma32(ga[kk], vf[kk], dp);
+      }
+      {
+        // 8 reads first, then the rest two by two between the products
+        constexpr int NR = 8 * C::CT + 8;          // reads in this region
+        constexpr int NM = 2 * C::KS;              // products in this region
+        constexpr int PER = (NR - 8 + NM - 1) / NM;
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // 0x100: LDS reads
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 0x008: MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Region B: softmax.
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = 4 * g + r;
+          float pe = fast_exp2(__builtin_fmaf(s[v], p.sl2, -l4[g][r]));
+          if (EDGE) {
+            const int row = row0 + 32 * it + 8 * g + 4 * hh + r;
+            if ((CAUSAL && mykey > row) || mykey >= N) pe = 0.f;
+          }
+          pv[v] = pe;
+          dsv[v] = pe * (dp[v] - d4[g][r]);
+        }
+      }
+      bf16x8 pk[2], dsk[2];
+      pk[0] = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+      pk[1] = to_bf16x8(pv[8], pv[9], pv[10], pv[11], pv[12], pv[13], pv[14], pv[15]);
+      dsk[0] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+      dsk[1] = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
+      // Block boundary: publish the next block before its rows are read.
+      bool more = true;
+      int nstage = stage;
+      if (it + 1 == C::IT) {
+        const int r3 = r2 < n_rb ? next_kept(r2) : n_rb;
+        more = r1 < n_rb;
+        if (more) {
+          wait_block(r2 < n_rb ? 1 : 0);
+          __syncthreads();
+          if (r3 < n_rb) issue(r3, (stage + 3) & 3);
+        }
+        nstage = (stage + 1) & 3;
+        r1 = r2;
+        r2 = r3;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Region C: dV/dK products, interleaved with the next sub-tile's row reads.
+#pragma unroll
+      for (int ct = 0; ct < C::CT; ++ct) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          dv[ct] = mfma32(ota[ct][h], pk[h], dv[ct]);
+          dk[ct] = mfma32(qta[ct][h], dsk[h], dk[ct]);
+        }
+      }
+      read_rows(nstage, it + 1 < C::IT ? it + 1 : 0);   // after the last block: unused
+      {
+        // one read of the next sub-tile's rows after each product
+        constexpr int NR = 2 * C::KS;
+        constexpr int NM = 4 * C::CT;
+        constexpr int PER = (NR + NM - 1) / NM;
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     stage = (stage + 1) & 3;
-    rb = r1;
-    r1 = r2;
-    r2 = r3;
   };
   // Blocks that need masking come first (the causal diagonal: rows below
   // key0 + BN - 1) or are all of them (the last key block when N is ragged);
-  // the rest run a copy of the body without any masking code.
+  // the rest run a copy of the body without any masking code. rb advances to
+  // the r1 the block leaves behind (r1 is shifted inside the block, so the
+  // value to advance to is saved first).
   auto edge_block = [&](int b) {
     return (CAUSAL && b * C::BM < key0 + C::BN - 1) || key0 + C::BN > N;
   };
-  while (rb < n_rb && edge_block(rb)) step(std::true_type{});
-  while (rb < n_rb) step(std::false_type{});
+  while (rb < n_rb && edge_block(rb)) {
+    const int nxt = r1;
+    block(std::true_type{});
+    rb = nxt;
+  }
+  while (rb < n_rb) {
+    const int nxt = r1;
+    block(std::false_type{});
+    rb = nxt;
+  }
 
   // dK^T / dV^T accumulators: lane holds key mykey, columns 32*ct + 8*g + 4*hh + r.
   if (mykey < N) {
