@@ -81,19 +81,35 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest() -> str:
+# The sources each measured kernel is built from (its own file, the shared
+# device header, the launch interface and the C ABI): a traffic record is valid
+# only while these are unchanged.
+COMMON_SOURCES = ("fa_api.hip", "fa_common.hpp", "fa_kernels.hpp")
+KERNEL_FILE = {"fa_fwd_kernel": "fa_fwd.hip", "fa_bwd_pre_kernel": "fa_bwd.hip",
+               "fa_bwd_dkdv_kernel": "fa_bwd.hip", "fa_bwd_dq_kernel": "fa_bwd_dq.hip",
+               "softmax_rows_reg": "fa_softmax.hip", "softmax_rows_stream": "fa_softmax.hip",
+               "fa_decode_split_kernel": "fa_decode.hip"}
+
+
+def source_digest(files=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in files:
         with open(os.path.join(ROOT, "exact_io_aware_61_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def kernel_digest(kernel: str) -> str:
+    """Digest of the sources one kernel is built from."""
+    return source_digest((KERNEL_FILE[kernel],) + COMMON_SOURCES)
 
 
 def traffic_record(kernel: str, workload: str, digest: str):
     """HBM bytes per launch from a committed counter summary, if it was taken on this source.
 
     profiles/traffic_<kernel>_<workload>.md holds a line
-    `traffic-record: {"src": "<digest>", "bytes_per_launch": X, ...}`.
+    `traffic-record: {"src": "<digest>", "bytes_per_launch": X, ...}`, where the digest
+    is kernel_digest(kernel) of the sources the counters were taken on.
     """
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
     if not os.path.exists(path):
@@ -194,7 +210,7 @@ def bench_softmax(args):
     value = nbytes / (wall / K) / 1e9
     kname = "softmax_rows_reg" if (cols % 4 == 0 and cols <= 4096) else "softmax_rows_stream"
     digest = source_digest()
-    rec = traffic_record(kname, f"{rows}x{cols}", digest)
+    rec = traffic_record(kname, f"{rows}x{cols}", kernel_digest(kname))
     result = {
         "metric": "row softmax GB/s (one read + one write per element)", "value": round(value, 2),
         "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -281,7 +297,7 @@ def bench_decode(args):
     achieved = nbytes / (per_ms * 1e-3) / 1e9
     digest = source_digest()
     shape = f"{B}x{H}x{Nq}x{Nk}x{d}"
-    rec = traffic_record("fa_decode_split_kernel", shape, digest)
+    rec = traffic_record("fa_decode_split_kernel", shape, kernel_digest("fa_decode_split_kernel"))
     result = {
         "metric": "decode GB/s (K, V, Q read and O, LSE written once)",
         "value": round(nbytes / (wall / K) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -528,7 +544,7 @@ def main():
     dom = max(kernel_flop, key=lambda n: per[n])
     achieved = kernel_flop[dom] / (per[dom] * 1e-3) / 1e12
     digest = source_digest()
-    rec = traffic_record(dom, w.name, digest)
+    rec = traffic_record(dom, w.name, kernel_digest(dom))
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
