@@ -62,8 +62,16 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a0, float a1, float a2, float 
   return __builtin_convertvector(x, bf16x4);
 }
 
-// Exchange with the lane 32 away (the other half of the wave).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+// Exchange with the lane 32 away (the other half of the wave). v_permlane32_swap
+// exchanges the upper half of its first operand with the lower half of its
+// second; with both holding x, the lower lanes of the second result and the
+// upper lanes of the first hold the other half's values. Two VALU operations,
+// no trip through LDS as with a general lane shuffle.
+__device__ __forceinline__ float swap_halves(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (__lane_id() & 32) ? r[0] : r[1]);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -223,12 +223,17 @@ void fa_fwd_kernel(FwdParams p) {
         }
       }
     }
-    float mx = -INFINITY;
+    // Row max as two chains of three-input maxima (v_max3_f32: two scores per step).
+    float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
     for (int st = 0; st < C::NT; ++st) {
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[st][v], s[st][v + 1]));
+      for (int v = 0; v < 16; v += 4) {
+        m0 = fmaxf(fmaxf(m0, s[st][v]), s[st][v + 1]);
+        m1 = fmaxf(fmaxf(m1, s[st][v + 2]), s[st][v + 3]);
+      }
     }
+    float mx = fmaxf(m0, m1);
     mx = fmaxf(mx, swap_halves(mx)) * p.sl2;
     // Move the reference max only if some row of this wave outgrew it by > 2^8.
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold) != 0) {
