@@ -236,17 +236,37 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   // (rows past N clamped; their L2 is +inf) and the block's L2 and D rows, one
   // 256-byte load each by the first 2*SROWS waves.
   const bool row_loader = wave < 2 * C::SROWS;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar address math
+  const uint32_t lds0 = lds_byte_addr(smem);
+  uint32_t soff[C::SPW];   // byte offsets of this lane's chunks, the same for every block
+#pragma unroll
+  for (int i = 0; i < C::SPW; ++i) soff[i] = slot_offset<C::C>(wave + i * C::WAVES, lane, 2 * D);
   auto issue = [&](int rb, int stage) {
     const int row0 = rb * C::BM;
     bf16* Qs = smem + stage * C::STAGE;
     bf16* dOs = Qs + C::TILE;
     float* Rs = reinterpret_cast<float*>(dOs + C::TILE);
+    if (row0 + C::BM <= N) {
+      // whole block inside the sequence: scalar base, fixed lane offsets
+      const bf16* qb = Qh + (int64_t)row0 * D;
+      const bf16* gb = dOh + (int64_t)row0 * D;
+      const uint32_t qdst = lds0 + 2u * (uint32_t)(stage * C::STAGE);
 #pragma unroll
-    for (int i = 0; i < C::SPW; ++i) {
-      const int slot = wave + i * C::WAVES;
-      dma_slot<C::C>(Qs, slot, lane, [&](int r) { return Qh + (int64_t)min(row0 + r, N - 1) * D; });
-      dma_slot<C::C>(dOs, slot, lane,
-                     [&](int r) { return dOh + (int64_t)min(row0 + r, N - 1) * D; });
+      for (int i = 0; i < C::SPW; ++i) {
+        const uint32_t o = 2u * 512u * (uint32_t)(uwave + i * C::WAVES);
+        dma16_s(soff[i], qb, qdst + o);
+        dma16_s(soff[i], gb, qdst + 2u * C::TILE + o);
+      }
+    } else {
+      // the ragged last block: rows past N clamped to the last row
+#pragma unroll
+      for (int i = 0; i < C::SPW; ++i) {
+        const int slot = wave + i * C::WAVES;
+        dma_slot<C::C>(Qs, slot, lane,
+                       [&](int r) { return Qh + (int64_t)min(row0 + r, N - 1) * D; });
+        dma_slot<C::C>(dOs, slot, lane,
+                       [&](int r) { return dOh + (int64_t)min(row0 + r, N - 1) * D; });
+      }
     }
     if (row_loader) {
       const int arr = wave / C::SROWS;   // 0: L2, 1: D

@@ -151,17 +151,37 @@ void fa_bwd_dq_kernel(DqParams p) {
   }
 
   // Direct global->LDS loads of one K/V tile into a stage (keys past N clamped).
+  // Byte offsets of this lane's chunks in its slots, the same for every tile.
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);   // uniform: scalar address math
+  const uint32_t lds0 = lds_byte_addr(smem);
+  uint32_t soff[C::SPW];
+#pragma unroll
+  for (int i = 0; i < C::SPW; ++i) soff[i] = slot_offset<C::C>(wave + i * C::WAVES, lane, 2 * D);
   auto issue = [&](int kt, int stage) {
     bf16* Ks = smem + stage * C::STAGE;
     bf16* Vs = Ks + C::TILE;
     const int key0 = kt * C::BN;
+    if (key0 + C::BN <= N) {
+      // whole tile inside the sequence: scalar base, fixed lane offsets
+      const bf16* kb = Kh + (int64_t)key0 * D;
+      const bf16* vb = Vh + (int64_t)key0 * D;
+      const uint32_t kdst = lds0 + 2u * (uint32_t)(stage * C::STAGE);
 #pragma unroll
-    for (int i = 0; i < C::SPW; ++i) {
-      const int slot = wave + i * C::WAVES;
-      dma_slot<C::C>(Ks, slot, lane,
-                     [&](int r) { return Kh + (int64_t)min(key0 + r, N - 1) * D; });
-      dma_slot<C::C>(Vs, slot, lane,
-                     [&](int r) { return Vh + (int64_t)min(key0 + r, N - 1) * D; });
+      for (int i = 0; i < C::SPW; ++i) {
+        const uint32_t o = 2u * 512u * (uint32_t)(uwave + i * C::WAVES);
+        dma16_s(soff[i], kb, kdst + o);
+        dma16_s(soff[i], vb, kdst + 2u * C::TILE + o);
+      }
+    } else {
+      // the ragged last tile: keys past N clamped to the last key
+#pragma unroll
+      for (int i = 0; i < C::SPW; ++i) {
+        const int slot = wave + i * C::WAVES;
+        dma_slot<C::C>(Ks, slot, lane,
+                       [&](int r) { return Kh + (int64_t)min(key0 + r, N - 1) * D; });
+        dma_slot<C::C>(Vs, slot, lane,
+                       [&](int r) { return Vh + (int64_t)min(key0 + r, N - 1) * D; });
+      }
     }
   };
 

@@ -144,6 +144,33 @@ __device__ __forceinline__ void dma_slot(bf16* tile, int slot, int lane, RowPtr 
   dma16(row_ptr(r) + 8 * c, tile + slot * 512);
 }
 
+// The same direct load with a uniform 64-bit base in SGPRs, a 32-bit per-lane
+// byte offset (the global_load "saddr" form) and the LDS destination as a
+// uniform byte address: the offset of a slot is fixed for the whole sweep, so
+// the per-tile address work is scalar.
+__device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_byte), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ location (for dma16_s).
+__device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
+}
+
+// Byte offset, from the start of the tile's first source row, of the chunk that
+// lane l fills in slot `slot` of a swizzled tile with rows of C chunks and
+// `row_bytes` between source rows (the mapping of dma_slot).
+template <int C>
+__device__ __forceinline__ uint32_t slot_offset(int slot, int lane, int row_bytes) {
+  const int pos = slot * 64 + lane;
+  const int r = pos / C;
+  const int c = (pos % C) ^ swz<C>(r);
+  return (uint32_t)(r * row_bytes + 16 * c);
+}
+
 // Block-mask bits staged in LDS: one 128-row mask row (or column) is at most
 // kMaxMaskBlocks entries, so N <= 128 * kMaxMaskBlocks when a block mask is used.
 constexpr int kMaxMaskBlocks = 16384;
