@@ -98,6 +98,9 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, mask=ctypes.byref(bad_block)) == MASK
     neg_stride = FaMask(2, 128, 0x90000, -1)
     assert fwd(lib, mask=ctypes.byref(neg_stride)) == MASK
+    # a block mask covers at most 16384 blocks of 128: N <= 2^21
+    grid = FaMask(2, 128, 0x90000, 0)
+    assert fwd(lib, mask=ctypes.byref(grid), N=(1 << 21) + 1, B=1, H=1) == MASK
 
 
 def test_zero_extent_returns_ok_without_pointers(lib):
