@@ -59,6 +59,9 @@ struct FwdCfg {
   static constexpr int SPW = SLOTS / WAVES;       // ... per wave
   static constexpr int LPT = 2 * SPW;             // direct loads per thread per K+V tile
   static constexpr int NMR = BM / 128;            // block-mask rows per workgroup
+  // K operands are read this many k-steps ahead of their products. At d=64 a
+  // deeper lead would push the register count past 128 and halve occupancy.
+  static constexpr int KPRE = D == 128 ? 4 : 1;
   static_assert(SLOTS % WAVES == 0, "tile slots split evenly over waves");
 };
 
@@ -223,12 +226,28 @@ void fa_fwd_kernel(FwdParams p) {
     f32x16 s[C::NT];
 #pragma unroll
     for (int st = 0; st < C::NT; ++st) s[st] = f32x16{};
+    // The reads of k-step kk + KPRE are issued behind the products of k-step kk
+    // (a rotating set of KPRE + 1 operand registers), so every product finds
+    // its operand loaded instead of waiting out an LDS round trip.
+    constexpr int KPRE = C::KPRE;
+    bf16x8 ka[KPRE + 1][C::NT];
+#pragma unroll
+    for (int kk = 0; kk < KPRE; ++kk)
+#pragma unroll
+      for (int st = 0; st < C::NT; ++st) ka[kk][st] = lds_b128(Ks + koff[kk] + 32 * st * D);
+    if (KPRE > 1) __builtin_amdgcn_sched_group_barrier(0x100, C::NT * KPRE, 0);   // DS reads
 #pragma unroll
     for (int kk = 0; kk < C::KS; ++kk) {
 #pragma unroll
-      for (int st = 0; st < C::NT; ++st) {
-        const bf16x8 a = lds_b128(Ks + koff[kk] + 32 * st * D);
-        s[st] = mfma32(a, qf[kk], s[st]);
+      for (int st = 0; st < C::NT; ++st) s[st] = mfma32(ka[kk % (KPRE + 1)][st], qf[kk], s[st]);
+      if (kk + KPRE < C::KS) {
+#pragma unroll
+        for (int st = 0; st < C::NT; ++st)
+          ka[(kk + KPRE) % (KPRE + 1)][st] = lds_b128(Ks + koff[kk + KPRE] + 32 * st * D);
+      }
+      if (KPRE > 1) {
+        __builtin_amdgcn_sched_group_barrier(0x008, C::NT, 0);                   // MFMA
+        if (kk + KPRE < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, C::NT, 0);
       }
     }
     // s[st][v] is the score of query qrow and key kbase + 32*st + 8*(v/4) + 4*hh + v%4.
