@@ -1,0 +1,77 @@
+"""Checks on the gfx950 assembly of every kernel source (CPU only: hipcc cross-compiles).
+
+* `m0` is written only by the direct global->LDS loads of fa_common.hpp, each
+  immediately before its load (the inline assembly lists `m0` as clobbered, and
+  no compiler-generated code may hold a value in it across those statements);
+* no packed FP32 VALU instruction appears (the build turns the feature off);
+* no kernel spills registers or uses scratch memory.
+"""
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from exact_io_aware_61_amd import build as fab
+
+SOURCES = [s for s in fab.SOURCES if s != "fa_api.hip"]
+
+
+@pytest.fixture(scope="module")
+def asm():
+    try:
+        hipcc = fab.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    out = {}
+    with tempfile.TemporaryDirectory() as d:
+        procs = []
+        for src in SOURCES:
+            path = os.path.join(d, src + ".s")
+            cmd = [hipcc, *fab.DEVICE_FLAGS, "-I", fab.INCLUDE, "-I", fab.CSRC, "--cuda-device-only",
+                   "-S", os.path.join(fab.CSRC, src), "-o", path]
+            procs.append((src, path, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                      stderr=subprocess.PIPE, text=True)))
+        for src, path, p in procs:
+            _, err = p.communicate()
+            assert p.returncode == 0, f"{src}: {err[-2000:]}"
+            with open(path) as f:
+                out[src] = f.read()
+    return out
+
+
+def _code_lines(text):
+    for line in text.split("\n"):
+        s = line.strip()
+        if not s or s.startswith(";") or s.startswith(".") or s.endswith(":"):
+            continue
+        yield s
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_m0_written_only_for_direct_loads(asm, src):
+    lines = list(_code_lines(asm[src]))
+    for i, s in enumerate(lines):
+        if re.search(r"\bm0\b", s):
+            assert s.startswith("s_mov_b32 m0,"), f"{src}: unexpected use of m0: {s}"
+            assert i + 1 < len(lines) and lines[i + 1].startswith("global_load_lds_"), \
+                f"{src}: m0 set without a direct load after it: {s} / {lines[i + 1]}"
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_packed_fp32(asm, src):
+    bad = [s for s in _code_lines(asm[src]) if re.match(r"v_pk_(add|mul|fma)_f32\b", s)]
+    assert not bad, f"{src}: {bad[:3]}"
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_spills_or_scratch(asm, src):
+    text = asm[src]
+    names = re.findall(r"^\s+\.name:\s+(\S+)", text, re.M)
+    for key in ("vgpr_spill_count", "sgpr_spill_count", "private_segment_fixed_size"):
+        vals = [int(v) for v in re.findall(rf"^\s+\.{key}:\s+(\d+)", text, re.M)]
+        assert vals, f"{src}: no {key} in the kernel metadata"
+        if key == "sgpr_spill_count":
+            continue   # SGPR spills go to VGPR lanes, not memory
+        assert all(v == 0 for v in vals), f"{src}: {key} {list(zip(names, vals))}"
