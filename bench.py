@@ -23,6 +23,11 @@ float32 matrix (--softmax-shape ROWSxCOLS) instead, in GB/s against HBM.
 --kernel decode times decoding against a KV cache (fa_decode) on
 --decode-shape BxHxNqxNkxd, in GB/s of the K/V stream against HBM.
 
+--kernel naive times standard attention on --workload, the comparator of the
+IO argument: S = Q K^T and P = softmax(S) materialised in device memory in
+bf16 by torch's GEMM and softmax (a measurement tool only, not part of the
+library), beside fa_fwd on the same inputs.
+
 --probe copy runs an elementwise kernel that reads and writes a buffer of known
 size, used to calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters.
 """
@@ -63,13 +68,16 @@ def parse():
                     help="run the workload with a 128x128 block mask of this keep probability "
                          "(off-diagonal blocks; the diagonal is always kept)")
     ap.add_argument("--causal", action="store_true", help="add the causal mask to the workload")
-    ap.add_argument("--kernel", choices=["attention", "softmax", "decode", "fwd-kv-outer"],
+    ap.add_argument("--kernel", choices=["attention", "softmax", "decode", "fwd-kv-outer",
+                                         "naive"],
                     default="attention",
                     help="attention: the fwd+bwd step (default); softmax: the standalone row "
                          "softmax (fa_softmax_rows) on --softmax-shape; decode: the newest "
                          "queries against a KV cache (fa_decode) on --decode-shape; "
                          "fwd-kv-outer: the forward in the K/V-outer loop order "
-                         "(fa_fwd_kv_outer) beside fa_fwd on --workload")
+                         "(fa_fwd_kv_outer) beside fa_fwd on --workload; naive: standard "
+                         "attention with S and P materialised (torch GEMM + softmax) beside "
+                         "fa_fwd on --workload")
     ap.add_argument("--decode-shape", default="4x32x16x32768x128",
                     help="BxHxNqxNkxd for --kernel decode (causal unless --decode-full)")
     ap.add_argument("--decode-full", action="store_true",
@@ -426,6 +434,115 @@ def bench_kv_outer(args):
     print(json.dumps(result), flush=True)
 
 
+def naive_io_model(N: int, d: int, masked: bool, heads: int) -> dict:
+    """Device bytes of the materialised standard attention, counted from its passes.
+
+    Per head (bf16): K^T made contiguous (read and write K), Q scaled (read and
+    write Q), S = Q K^T (read Q, K^T; write S), the mask applied in place (read
+    and write S), P = softmax(S) (read S, write P), O = P V (read P, V; write O).
+    The S and P terms are the Theta(N^2) of standard attention; the mask pass
+    reads a [N, N] bool shared by all heads, not counted here.
+    """
+    nd, nn = 2 * N * d, 2 * N * N
+    per_head = (2 * nd) + (2 * nd) + (2 * nd + nn) + (2 * nn if masked else 0) + 2 * nn \
+        + (nn + 2 * nd)
+    return {"naive_model": float(heads * per_head),
+            "naive_s_p_bytes": float(heads * (nn * (5 if masked else 3)))}
+
+
+def bench_naive(args):
+    """Standard attention with S and P in device memory, and fa_fwd, on one workload.
+
+    One naive step: K^T made contiguous, Q scaled, S = Q K^T (bf16 out), the
+    causal or block mask written into S as -inf, P = softmax(S) (bf16), O = P V.
+    Both paths are timed with HIP events on the stream they run on. The naive
+    O is compared with fa_fwd's O (max abs difference, reported).
+    """
+    import numpy as np
+    import torch
+
+    import exact_io_aware_61_amd as fa
+    from exact_io_aware_61_amd.workloads import WORKLOADS, kept_fraction, make_inputs, variant
+    w = WORKLOADS[args.workload]
+    if args.block_keep is not None or args.causal:
+        w = variant(w, block_keep=args.block_keep, causal=True if args.causal else None)
+    print(f"[bench] naive vs fa_fwd on {w.name}", file=sys.stderr, flush=True)
+    q, k, v, _, bm = make_inputs(w, with_do=False)
+    dev = torch.device("cuda:0")
+    qg, kg, vg = (t.to(dev) for t in (q, k, v))
+    # The mask as a dense [N, N] bool (True = dropped), built on the CPU and
+    # copied once: an input of the naive path, like the block grid of fa_fwd.
+    drop = None
+    if w.causal or bm is not None:
+        dm = torch.zeros((w.N, w.N), dtype=torch.bool)
+        if w.causal:
+            dm |= torch.ones((w.N, w.N), dtype=torch.bool).triu(1)
+        if bm is not None:
+            full = torch.from_numpy(bm).bool().repeat_interleave(128, 0).repeat_interleave(128, 1)
+            dm |= ~full[:w.N, :w.N]
+        drop = dm.to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def naive():
+        kt = kg.transpose(-1, -2).contiguous()
+        s = torch.matmul(qg * w.scale, kt)
+        if drop is not None:
+            s.masked_fill_(drop, float("-inf"))
+        pm = torch.softmax(s, dim=-1)
+        del s
+        return torch.matmul(pm, vg)
+
+    o = torch.empty_like(qg)
+    lse = torch.empty((w.B, w.H, w.N), device=dev, dtype=torch.float32)
+    grid = None if bm is None else torch.from_numpy(bm).to(dev)
+
+    def flash():
+        fa.forward(qg, kg, vg, causal=w.causal, block_mask=grid, scale=w.scale, out=o, lse=lse)
+
+    def timed(f, steps, warmup):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            f()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+
+    t_naive = timed(naive, args.steps, args.warmup)
+    print(f"[bench] naive {t_naive:.4f} ms", file=sys.stderr, flush=True)
+    t_fa = timed(flash, args.steps, args.warmup)
+    print(f"[bench] fa_fwd {t_fa:.4f} ms", file=sys.stderr, flush=True)
+    o_naive = naive()
+    torch.cuda.synchronize()
+    diff = float((o_naive.float().cpu() - o.float().cpu()).abs().max())
+    rho = kept_fraction(w.N, w.causal, bm)
+    flop = 4.0 * w.B * w.H * w.N * w.N * w.d * rho
+    heads = w.B * w.H
+    br = 128 if bm is not None else 256
+    io = naive_io_model(w.N, w.d, drop is not None, heads)
+    io["fa_fwd_compulsory"] = float(heads * (8 * w.N * w.d + 4 * w.N))
+    io["fa_fwd_tile_model"] = float(heads * (4 * w.N * w.d + 4 * w.N * w.d * (-(-w.N // br)) * rho
+                                             + 4 * w.N))
+    result = {
+        "metric": "attention forward TFLOP/s, standard attention with S and P in HBM",
+        "value": round(flop / (t_naive * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_naive, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "mask": "causal" if w.causal else ("block" if bm is not None else "none"),
+                   "rho": round(rho, 6)},
+        "naive_ms": round(t_naive, 4), "fa_fwd_ms": round(t_fa, 4),
+        "fa_fwd_tflops": round(flop / (t_fa * 1e-3) / 1e12, 2),
+        "speedup_fa_fwd": round(t_naive / t_fa, 2), "max_abs_diff_o": diff,
+        "io_model_bytes": io, "roofline": None, "cpu_baseline": None, "src": source_digest(),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -455,6 +572,9 @@ def main():
         return
     if args.kernel == "fwd-kv-outer":
         bench_kv_outer(args)
+        return
+    if args.kernel == "naive":
+        bench_naive(args)
         return
 
     lib = fa.load()
