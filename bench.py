@@ -131,6 +131,26 @@ def traffic_record(kernel: str, workload: str, digest: str):
     return None
 
 
+def device_info(lib, device: int = 0):
+    """CU count and peak shader clock as the HIP runtime reports them, and the peak they give.
+
+    hipDeviceGetAttribute is looked up through libfa.so, so it is the runtime the
+    kernels run on. Attribute codes from ROCm 7's hip_runtime_api.h:
+    hipDeviceAttributeClockRate = 5 (kHz), hipDeviceAttributeMultiprocessorCount = 63.
+    """
+    try:
+        get = lib.hipDeviceGetAttribute
+    except AttributeError:
+        return None
+    get.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    khz, cus = ctypes.c_int(0), ctypes.c_int(0)
+    if get(ctypes.byref(khz), 5, device) != 0 or get(ctypes.byref(cus), 63, device) != 0:
+        return None
+    return {"cus": cus.value, "peak_clock_mhz": khz.value / 1000.0,
+            "bf16_peak_tflops": round(cus.value * 4096 * khz.value * 1e3 / 1e12, 1),
+            "formula": "CUs x 4096 dense bf16 FLOP/clk per CU x peak clock"}
+
+
 def probe_copy(mib: int, steps: int):
     import torch
     n = mib * (1 << 20) // 4
@@ -701,6 +721,7 @@ def main():
         "kernel_ms": {n: round(t, 4) for n, t in per.items()},
         "roofline": roofline,
         "io_bytes": {k: (int(v) if k != "rows_per_workgroup_fwd" else v) for k, v in io.items()},
+        "device": device_info(lib, dev.index or 0),
         "src": digest,
     }
     if args.cpu_seconds > 0:
