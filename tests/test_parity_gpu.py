@@ -101,6 +101,27 @@ def test_per_head_block_masks():
     assert_parity(gpu, ref, label="per-head masks")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_mask_head_major_order(d, causal):
+    """B*H a multiple of 8 with a block mask: the launches take the head-major
+    workgroup order (each XCD works through whole heads); every head, with a
+    grid of its own, is compared in full, on a ragged N."""
+    B, H, N = 2, 8, 600
+    q, k, v, do = make_qkv(B, H, N, d, seed=34 + d)
+    nb = -(-N // 128)
+    rng = np.random.default_rng(35 + d)
+    grids = (rng.random((B, H, nb, nb)) < 0.5).astype(np.uint8)
+    for b in range(B):
+        for h in range(H):
+            np.fill_diagonal(grids[b, h], 1)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    print(f"[case] head-major block order d={d} causal={causal}", flush=True)
+    gpu = run_gpu(q, k, v, do, causal=causal, block_mask=grids, scale=scale)
+    ref = run_oracle(q, k, v, do, causal=causal, block_mask=grids, scale=scale)
+    assert_parity(gpu, ref, label=f"head-major d={d} causal={causal}")
+
+
 def test_empty_rows_from_block_mask():
     """Rows whose every block is dropped: O = 0, LSE = -inf, zero gradients."""
     N, d = 256, 64
