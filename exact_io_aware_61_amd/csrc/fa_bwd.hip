@@ -19,7 +19,7 @@
 //
 // dK/dV kernel, per workgroup of 4 waves = 128 keys; wave w owns keys
 // key0 + 32w .. +31, keeps their K and V rows in VGPRs and their dK^T, dV^T
-// accumulators on chip. Per block of BM query rows (the Q and dO tiles and the
+// accumulators on chip. Per block of 64 query rows (the Q and dO tiles and the
 // rows' L2 and D reach LDS by direct global->LDS loads, 2-3 blocks ahead),
 // per wave and 32-row sub-tile:
 //   S  = Q K_w^T, dP = dO V_w^T   MFMA 32x32x16, Q/dO rows by 16-byte LDS reads;
@@ -99,7 +99,11 @@ struct BwdCfg {
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BN = 32 * WAVES;           // keys per workgroup (= block-mask granularity)
-  static constexpr int BM = D == 128 ? 64 : 128;  // query rows per block
+  // Query rows per block. 64 at both head dims: at d=64 that keeps the
+  // four-stage ring at 68 KiB, so two workgroups share a CU and each SIMD runs
+  // two waves (one wave's softmax under the other's products); at d=128 the
+  // registers allow one wave per SIMD whatever the ring.
+  static constexpr int BM = 64;
   static constexpr int IT = BM / 32;              // 32-row sub-tiles
   static constexpr int KS = D / 16;               // 16-column MFMA k-steps over the head dim
   static constexpr int CT = D / 32;               // 32-column sub-tiles of the head dim
@@ -135,7 +139,7 @@ struct BwdParams {
 };
 
 template <int D, bool CAUSAL, bool BLOCK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   // [stage][Q tile, dO tile, L2 rows, D rows]
@@ -276,8 +280,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // Software pipeline over 32-row sub-tiles, one wave per SIMD, so the wave's
-  // own instruction order decides what overlaps. At the start of a sub-tile
+  // Software pipeline over 32-row sub-tiles. At d=128 there is one wave per
+  // SIMD, so the wave's own instruction order decides what overlaps (at d=64 a
+  // second workgroup's wave shares the SIMD). At the start of a sub-tile
   // its Q/dO row operands are already in registers (read during the previous
   // sub-tile's dV/dK products); its transposed operands and row statistics
   // are read between its S/dP products, two reads per product; after the
