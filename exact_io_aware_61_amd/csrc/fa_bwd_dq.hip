@@ -34,8 +34,11 @@ namespace {
 template <int D, bool BLOCK>
 struct DqCfg {
   // A block mask works on 128-row blocks: masked launches use 128-row
-  // workgroups so that every wave of a workgroup keeps the same tiles.
-  static constexpr int WAVES = BLOCK ? 4 : 8;
+  // workgroups so that every wave of a workgroup keeps the same tiles. At d=64
+  // every launch does: the kernel fits in 168 registers and a 48 KiB ring, so
+  // three 4-wave workgroups share a CU (three waves per SIMD), where 8-wave
+  // workgroups would leave it at two.
+  static constexpr int WAVES = (BLOCK || D == 64) ? 4 : 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;           // query rows per workgroup
   static constexpr int BN = 64;                   // keys per K/V tile
