@@ -113,10 +113,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 // the compiler does not treat it as an LDS store and add waits before later
 // LDS reads of other buffers; the kernels order these loads themselves (wait
 // for the vector-memory counter, then a workgroup barrier, before any read).
+// A scalar write of m0 needs one wait state before an LDS-DMA load reads it;
+// the hazard recognizer cannot see into an asm block, so the s_nop is written
+// out here (the compiler emits the same nop for its own global_load_lds).
 __device__ __forceinline__ void dma16(const void* src, const bf16* lds_dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds_dst));
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(lds), "v"(src)
                : "memory", "m0");
@@ -127,7 +130,7 @@ __device__ __forceinline__ void dma16(const void* src, const bf16* lds_dst) {
 __device__ __forceinline__ void dma4(const void* src, const void* lds_dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds_dst));
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :
                : "s"(lds), "v"(src)
                : "memory", "m0");
@@ -149,7 +152,7 @@ __device__ __forceinline__ void dma_slot(bf16* tile, int slot, int lane, RowPtr 
 // uniform byte address: the offset of a slot is fixed for the whole sweep, so
 // the per-tile address work is scalar.
 __device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds_byte) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(lds_byte), "v"(voff), "s"(sbase)
                : "memory", "m0");

@@ -1,8 +1,11 @@
 """Checks on the gfx950 assembly of every kernel source (CPU only: hipcc cross-compiles).
 
 * `m0` is written only by the direct global->LDS loads of fa_common.hpp, each
-  immediately before its load (the inline assembly lists `m0` as clobbered, and
-  no compiler-generated code may hold a value in it across those statements);
+  followed by exactly one `s_nop 0` and then its load: an SALU write of m0
+  needs one wait state before an LDS-DMA load consumes it, and the hazard
+  recognizer does not look inside asm blocks (the inline assembly lists `m0`
+  as clobbered, and no compiler-generated code may hold a value in it across
+  those statements);
 * no packed FP32 VALU instruction appears (the build turns the feature off);
 * no kernel spills registers or uses scratch memory.
 """
@@ -55,8 +58,10 @@ def test_m0_written_only_for_direct_loads(asm, src):
     for i, s in enumerate(lines):
         if re.search(r"\bm0\b", s):
             assert s.startswith("s_mov_b32 m0,"), f"{src}: unexpected use of m0: {s}"
-            assert i + 1 < len(lines) and lines[i + 1].startswith("global_load_lds_"), \
-                f"{src}: m0 set without a direct load after it: {s} / {lines[i + 1]}"
+            assert i + 2 < len(lines) and lines[i + 1] == "s_nop 0", \
+                f"{src}: m0 write not followed by a wait state: {s} / {lines[i + 1]}"
+            assert lines[i + 2].startswith("global_load_lds_"), \
+                f"{src}: m0 set without a direct load after it: {s} / {lines[i + 2]}"
 
 
 @pytest.mark.parametrize("src", SOURCES)
