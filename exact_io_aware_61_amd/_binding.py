@@ -96,6 +96,30 @@ def _shape(q: torch.Tensor, *others):
     return tuple(int(x) for x in q.shape)
 
 
+def _like(t, shape, dtype, device, name: str):
+    """A caller-supplied output (or the lse input): contiguous, of this shape and dtype,
+    on this GPU. Checked before anything is launched: a wrong pointer here would
+    reach the kernels as an out-of-bounds or host address."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}"
+                         f"{'' if t.is_contiguous() else ' (non-contiguous)'}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must live on {device}, got {t.device}")
+    return t
+
+
+def _ws_bytes(ws, device) -> int:
+    """Size in bytes of a caller-supplied workspace tensor (any dtype), on this GPU."""
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != device:
+        raise ValueError(f"the workspace must be a tensor on {device}")
+    if not ws.is_contiguous():
+        raise ValueError("the workspace must be contiguous")
+    return int(ws.numel()) * int(ws.element_size())
+
+
 def _mask(causal: bool, block_mask, B: int, H: int, N: int, device):
     """Build the fa_mask_t (or None) and keep the grid tensor alive alongside it."""
     kind = FA_MASK_CAUSAL if causal else 0
@@ -126,8 +150,10 @@ def forward(q, k, v, *, causal: bool = False, block_mask=None, scale: float | No
     """(o, lse) = attention forward. q, k, v: [B, H, N, d] bf16 on one GPU."""
     B, H, N, d = _shape(q, k, v)
     scale = default_scale(d) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
+    o = torch.empty_like(q) if out is None else _like(out, q.shape, torch.bfloat16, q.device,
+                                                         "out")
+    lse = (torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None
+           else _like(lse, (B, H, N), torch.float32, q.device, "lse"))
     mptr, keep = _mask(causal, block_mask, B, H, N, q.device)
     _check(load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, scale, mptr,
                          _stream(q)))
@@ -151,13 +177,17 @@ def backward(q, k, v, o, lse, do, *, causal: bool = False, block_mask=None,
     """(dq, dk, dv) for upstream gradient do, recomputing P from lse."""
     B, H, N, d = _shape(q, k, v, o, do)
     scale = default_scale(d) if scale is None else float(scale)
+    _like(lse, (B, H, N), torch.float32, q.device, "lse")
     ws = workspace(q) if ws is None else ws
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    ws_bytes = _ws_bytes(ws, q.device)
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        outs.append(torch.empty_like(q) if t is None
+                    else _like(t, q.shape, torch.bfloat16, q.device, name))
+    dq, dk, dv = outs
     mptr, keep = _mask(causal, block_mask, B, H, N, q.device)
     _check(load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
-                         _ptr(dk), _ptr(dv), B, H, N, d, scale, mptr, _ptr(ws), ws.numel(),
+                         _ptr(dk), _ptr(dv), B, H, N, d, scale, mptr, _ptr(ws), ws_bytes,
                          _stream(q)))
     del keep
     return dq, dk, dv
@@ -165,25 +195,31 @@ def backward(q, k, v, o, lse, do, *, causal: bool = False, block_mask=None,
 
 def bwd_preprocess(o, do, lse, ws):
     B, H, N, d = _shape(o, do)
+    _like(lse, (B, H, N), torch.float32, o.device, "lse")
     _check(load().fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(lse), B, H, N, d, _ptr(ws),
-                                    ws.numel(), _stream(o)))
+                                    _ws_bytes(ws, o.device), _stream(o)))
 
 
 def bwd_dkdv(q, k, v, do, dk, dv, ws, *, causal=False, block_mask=None, scale=None):
     B, H, N, d = _shape(q, k, v, do)
     scale = default_scale(d) if scale is None else float(scale)
+    _like(dk, q.shape, torch.bfloat16, q.device, "dk")
+    _like(dv, q.shape, torch.bfloat16, q.device, "dv")
+    ws_bytes = _ws_bytes(ws, q.device)
     mptr, keep = _mask(causal, block_mask, B, H, N, q.device)
     _check(load().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
-                              B, H, N, d, scale, mptr, _ptr(ws), ws.numel(), _stream(q)))
+                              B, H, N, d, scale, mptr, _ptr(ws), ws_bytes, _stream(q)))
     del keep
 
 
 def bwd_dq(q, k, v, do, dq, ws, *, causal=False, block_mask=None, scale=None):
     B, H, N, d = _shape(q, k, v, do)
     scale = default_scale(d) if scale is None else float(scale)
+    _like(dq, q.shape, torch.bfloat16, q.device, "dq")
+    ws_bytes = _ws_bytes(ws, q.device)
     mptr, keep = _mask(causal, block_mask, B, H, N, q.device)
     _check(load().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq),
-                            B, H, N, d, scale, mptr, _ptr(ws), ws.numel(), _stream(q)))
+                            B, H, N, d, scale, mptr, _ptr(ws), ws_bytes, _stream(q)))
     del keep
 
 
@@ -216,10 +252,13 @@ def decode(q, k, v, *, causal: bool = False, scale: float | None = None, ws=None
     _check(load().fa_decode_workspace_size(B, H, Nq, Nk, d, ctypes.byref(n)))
     if ws is None:
         ws = torch.empty(max(n.value, 16), device=q.device, dtype=torch.uint8)
+    ws_bytes = _ws_bytes(ws, q.device)
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must live on the same GPU")
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
     _check(load().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, scale,
-                            1 if causal else 0, _ptr(ws), ws.numel(), _stream(q)))
+                            1 if causal else 0, _ptr(ws), ws_bytes, _stream(q)))
     return o, lse
 
 
