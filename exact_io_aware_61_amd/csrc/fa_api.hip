@@ -10,6 +10,9 @@
 namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+// Sequence lengths stay this far below 2^31 so that rounding N up to any tile
+// (at most 256 rows) stays inside int.
+constexpr int kMaxSeq = INT32_MAX - 1024;
 
 struct Shape {
   int B, H, N, d;
@@ -19,10 +22,12 @@ struct Shape {
 };
 
 int check_shape(const Shape& s) {
-  if (s.B < 0 || s.H < 0 || s.N < 0) return FA_ERR_SHAPE;
+  if (s.B < 0 || s.H < 0 || s.N < 0 || s.N > kMaxSeq) return FA_ERR_SHAPE;
   if (s.d != 64 && s.d != 128) return FA_ERR_SHAPE;
   if (s.bh() > INT32_MAX) return FA_ERR_SHAPE;
-  if (s.elems() >= kMaxElems) return FA_ERR_SHAPE;
+  // B*H*N*d can exceed 2^63 before the limit check (B*H and N up to 2^31 - 1 each)
+  if ((unsigned __int128)s.bh() * (unsigned)s.N * (unsigned)s.d >= (unsigned __int128)kMaxElems)
+    return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -73,7 +78,7 @@ bool any_overlap(const Range* outs, int n_out, const Range* ins, int n_in) {
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int padded_rows(int N) {
-  const int r = fa::bwd_row_padding();
+  const int r = fa::kBwdRowPad;
   return (N + r - 1) / r * r;
 }
 
@@ -150,9 +155,12 @@ int check_grad_stage(const void* q, const void* k, const void* v, const void* do
 
 // Decoding: shape checks and the workspace of the key split.
 int decode_shape(int B, int H, int Nq, int Nk, int d) {
-  if (B < 0 || H < 0 || Nq < 0 || Nq > 32 || Nk < 0) return FA_ERR_SHAPE;
+  if (B < 0 || H < 0 || Nq < 0 || Nq > 32 || Nk < 0 || Nk > kMaxSeq) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_SHAPE;
-  if ((int64_t)B * H * ((int64_t)Nk + Nq) * d >= (int64_t(1) << 40)) return FA_ERR_SHAPE;
+  if ((int64_t)B * H > INT32_MAX) return FA_ERR_SHAPE;
+  if ((unsigned __int128)((int64_t)B * H) * (uint64_t)((int64_t)Nk + Nq) * (unsigned)d >=
+      (unsigned __int128)kMaxElems)
+    return FA_ERR_SHAPE;
   return FA_OK;
 }
 size_t decode_ws_o(int64_t BH, int Nq, int Nk, int d) {
@@ -366,8 +374,13 @@ int fa_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* 
     const Range out[1] = {range(y, bytes)};
     if (any_overlap(out, 1, in, 1)) return FA_ERR_ALIAS;
   }
-  fa::SoftmaxArgs a{x, y, rows, cols};
-  return launched(fa::launch_softmax_rows(a, static_cast<hipStream_t>(stream)));
+  // Launches of at most kSoftmaxRowsPerLaunch rows each, in row order.
+  for (int64_t r0 = 0; r0 < rows; r0 += fa::kSoftmaxRowsPerLaunch) {
+    const int64_t n = rows - r0 < fa::kSoftmaxRowsPerLaunch ? rows - r0 : fa::kSoftmaxRowsPerLaunch;
+    const fa::SoftmaxArgs a{x + r0 * cols, y + r0 * cols, n, cols};
+    FA_TRY(launched(fa::launch_softmax_rows(a, static_cast<hipStream_t>(stream))));
+  }
+  return FA_OK;
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -39,8 +39,6 @@
 namespace fa {
 namespace {
 
-constexpr int kRowPad = 128;   // row arrays are padded per head to a multiple of this
-
 // ------------------------------------------------------------------------------------------------
 // Preprocess: D_i = sum_c dO_ic O_ic and L2_i = LSE_i log2(e), padded as above.
 
@@ -115,7 +113,7 @@ struct BwdCfg {
   static constexpr int SPW = SLOTS / WAVES;
   static constexpr int SROWS = BM / 64;           // 256-byte loads per row array
   static_assert(SLOTS % WAVES == 0, "tile slots split evenly over waves");
-  static_assert(kRowPad % BM == 0, "row padding covers whole row blocks");
+  static_assert(kBwdRowPad % BM == 0, "row padding covers whole row blocks");
   static_assert(2 * SROWS <= WAVES, "at most one row-array load per wave");
 };
 
@@ -530,8 +528,6 @@ hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
-
-int bwd_row_padding() { return kRowPad; }
 
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream) {
   PreParams p;

@@ -243,18 +243,6 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-void decode_split(int BH, int Nk, int* nsplit, int* chunk) {
-  // Enough waves to cover the chip several times over, chunks of at least
-  // eight 32-key tiles.
-  const int target = (2048 + BH - 1) / BH;
-  const int max_split = Nk > 0 ? (Nk + 255) / 256 : 1;
-  int ns = target < max_split ? target : max_split;
-  if (ns < 1) ns = 1;
-  int ch = Nk > 0 ? (Nk + ns - 1) / ns : 32;
-  ch = (ch + 31) / 32 * 32;
-  *chunk = ch;
-  *nsplit = Nk > 0 ? (Nk + ch - 1) / ch : 1;
-}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.d == 128)

@@ -40,13 +40,13 @@ struct BwdArgs {
   MaskArgs mask;
   float* dvec;   // workspace: D_i = dO_i . O_i, [BH][Np] (0 past N)
   float* l2;     // workspace: LSE_i log2(e), [BH][Np] (+inf past N and for empty rows)
-  int Np;        // N rounded up to bwd_row_padding()
+  int Np;        // N rounded up to kBwdRowPad
 };
 
 struct SoftmaxArgs {
   const float* x;
   float* y;
-  int64_t rows;   // 1 .. 2^31 - 1
+  int64_t rows;   // 1 .. kSoftmaxRowsPerLaunch
   int64_t cols;   // 1 .. 2^31 - 1
 };
 
@@ -66,8 +66,18 @@ struct DecodeArgs {
 };
 
 // Key split of the decoding kernels: nsplit chunks of `chunk` keys (a multiple
-// of 32) cover Nk.
-void decode_split(int BH, int Nk, int* nsplit, int* chunk);
+// of 32) cover Nk. Enough waves to cover the chip several times over, chunks
+// of at least eight 32-key tiles.
+inline void decode_split(int BH, int Nk, int* nsplit, int* chunk) {
+  const int target = (2048 + BH - 1) / BH;
+  const int max_split = Nk > 0 ? (Nk + 255) / 256 : 1;
+  int ns = target < max_split ? target : max_split;
+  if (ns < 1) ns = 1;
+  int ch = Nk > 0 ? (Nk + ns - 1) / ns : 32;
+  ch = (ch + 31) / 32 * 32;
+  *chunk = ch;
+  *nsplit = Nk > 0 ? (Nk + ch - 1) / ch : 1;
+}
 
 struct KvOuterArgs {
   const void* q;
@@ -84,7 +94,12 @@ struct KvOuterArgs {
 };
 
 // Row padding of the per-row arrays in the backward workspace.
-int bwd_row_padding();
+constexpr int kBwdRowPad = 128;
+
+// Rows of one row-softmax launch: the C ABI splits larger matrices into
+// launches of at most this many rows, so that no launch asks for more than
+// 2^31 work-items (the streaming kernel runs 1024 threads per row).
+constexpr int64_t kSoftmaxRowsPerLaunch = int64_t(1) << 21;
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);

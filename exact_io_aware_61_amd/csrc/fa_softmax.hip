@@ -179,6 +179,8 @@ hipError_t launch_reg(const SoftmaxArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_softmax_rows(const SoftmaxArgs& a, hipStream_t stream) {
+  // At most 2^21 rows: 2^31 work-items for the streaming kernel, 2^27 for the other.
+  if (a.rows < 1 || a.rows > kSoftmaxRowsPerLaunch) return hipErrorInvalidValue;
   const bool vec = (a.cols % 4) == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
   if (vec && a.cols <= 4096) {

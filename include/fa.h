@@ -26,7 +26,8 @@
  *              Inputs are read-only; outputs must not overlap any input.
  *   Alignment  data pointers must be 16-byte aligned.
  *   Limits     B, H, N >= 0 (a zero extent is a no-op that returns FA_OK);
- *              d in {64, 128}; scale finite and > 0; B*H*N*d < 2^40.
+ *              d in {64, 128}; scale finite and > 0; B*H*N*d < 2^40;
+ *              N <= 2^31 - 1025 (B*H <= 2^31 - 1 follows).
  *              N need not be a multiple of any tile size. With a block mask,
  *              ceil(N / 128) <= 16384 (N <= 2^21).
  *   Streams    `stream` is a hipStream_t passed as void* (NULL = default
@@ -181,7 +182,7 @@ int fa_fwd_kv_outer(const void* q, const void* k, const void* v, void* o, float*
  *   causal : 0 or 1 (other values: FA_ERR_MASK)
  *   workspace : DEVICE buffer of at least fa_decode_workspace_size() bytes,
  *               caller-owned, contents irrelevant on entry, overwritten
- * Limits: 0 <= Nq <= 32, Nk >= 0 (k and v may be NULL when Nk = 0),
+ * Limits: 0 <= Nq <= 32, 0 <= Nk <= 2^31 - 1025 (k and v may be NULL when Nk = 0),
  * d in {64, 128}, B*H*(Nq+Nk)*d < 2^40. Errors and streams as above; outputs
  * and workspace must not overlap each other or any input.
  */
@@ -202,7 +203,9 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
  *   y : output [rows, cols] float32, DEVICE pointer; y == x (in place) is
  *       allowed, any other overlap is FA_ERR_ALIAS
  *   rows, cols : 0 .. 2^31 - 1 each, rows * cols < 2^40 (either 0: no-op
- *                returning FA_OK); otherwise FA_ERR_SHAPE
+ *                returning FA_OK); otherwise FA_ERR_SHAPE. Matrices of more
+ *                than 2^21 rows are processed as several launches of at most
+ *                2^21 rows each, enqueued in row order on `stream`.
  * x and y must be 4-byte aligned; rows that are 16-byte aligned (cols a
  * multiple of 4, x and y 16-byte aligned) take the vectorised kernels.
  * Asynchronous on `stream` like every entry point.
