@@ -80,6 +80,34 @@ def make_qkv(B: int, H: int, N: int, d: int, seed: int, with_do: bool = True):
     return q, k, v, do
 
 
+def make_rising_scores(B: int, H: int, N: int, d: int, seed: int, *, q_lead: float = 16.0,
+                       k_ramp: float = 8.0, rising: float = 0.75, late_outliers: int = 0):
+    """Q, K, V, dO whose scores grow (or shrink) steadily along each query row.
+
+    The draws of make_qkv(B, H, N, d, seed), then head-dim component 0 replaced:
+    every query row gets +q_lead (probability `rising`, from its own generator,
+    seed + 7) or -q_lead there, and key j gets a ramp from -k_ramp to +k_ramp
+    over j = 0 .. N-1. The score of a +q_lead row then grows by about
+    2 * q_lead * k_ramp (times the softmax scale) from the first key to the
+    last, so the running row maximum of a tiled sweep keeps moving long after
+    the first tile; -q_lead rows peak at the first keys instead. With
+    late_outliers = n, the last n keys get component 0 equal to 3 * k_ramp: a
+    jump of the row maximum at the very end. All values are rounded to bf16
+    like every other input.
+    """
+    q, k, v, do = make_qkv(B, H, N, d, seed)
+    rng = np.random.default_rng(seed + 7)
+    sign = np.where(rng.random((B, H, N)) < rising, 1.0, -1.0).astype(np.float32)
+    qn = q.float().numpy()
+    kn = k.float().numpy()
+    qn[..., 0] = q_lead * sign
+    kn[..., 0] = np.linspace(-k_ramp, k_ramp, N, dtype=np.float32)[None, None, :]
+    if late_outliers:
+        kn[..., N - late_outliers:, 0] = 3.0 * k_ramp
+    return (torch.from_numpy(qn).to(torch.bfloat16), torch.from_numpy(kn).to(torch.bfloat16),
+            v, do)
+
+
 def variant(w: Workload, block_keep: float | None = None, causal: bool | None = None) -> Workload:
     """The workload with another block-mask keep probability and/or the causal mask added.
 
