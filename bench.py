@@ -163,11 +163,24 @@ def probe_copy(mib: int, steps: int):
                       "launches": steps}), flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (the architecture if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, q, k, v, do, bm, seconds: float):
-    """Time the oracle on whole heads (forward + backward) on the host cores.
+    """Time the oracle on whole heads on the host cores: forward + backward, then forward alone.
 
     Heads run one after another until `seconds` have passed (at least one head,
     at most all of them); the rate is the heads done over the time they took.
+    The forward alone then runs on the same heads, for at most `seconds / 2`.
     """
     import numpy as np
     import threadpoolctl
@@ -176,22 +189,31 @@ def cpu_baseline(w, q, k, v, do, bm, seconds: float):
 
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
                    if p.get("user_api") == "blas"] or [1])
-    done, dt = 0, 0.0
-    while done < w.B * w.H and (done == 0 or dt < seconds):
-        b, h = divmod(done, w.H)
-        qa, ka, va, da = (t[b, h].double().numpy() for t in (q, k, v, do))
-        t0 = time.perf_counter()
-        attention_head(qa, ka, va, da, scale=w.scale, causal=w.causal, block_mask=bm)
-        dt += time.perf_counter() - t0
-        done += 1
+
+    def run(with_grad: bool, budget: float, limit: int):
+        done, dt = 0, 0.0
+        while done < limit and (done == 0 or dt < budget):
+            b, h = divmod(done, w.H)
+            qa, ka, va, da = (t[b, h].double().numpy() for t in (q, k, v, do))
+            t0 = time.perf_counter()
+            attention_head(qa, ka, va, da if with_grad else None, scale=w.scale,
+                           causal=w.causal, block_mask=bm)
+            dt += time.perf_counter() - t0
+            done += 1
+        return done, dt
+
+    done, dt = run(True, seconds, w.B * w.H)
+    fdone, fdt = run(False, seconds / 2, done)
     rho = kept_fraction(w.N, w.causal, bm)
-    flops = 3.5 * 4.0 * w.N * w.N * w.d * rho * done
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+    fwd_head = 4.0 * w.N * w.N * w.d * rho
+    return {"value": 3.5 * fwd_head * done / dt / 1e12, "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {w.B * w.H} heads of {w.name}, forward+backward, fp64 "
                       f"NumPy with S and P materialised, {dt:.2f} s",
-            "seconds": dt, "cpu": platform.processor() or platform.machine(),
-            "host_cpus": os.cpu_count()}
+            "seconds": dt,
+            "fwd": {"value": fwd_head * fdone / fdt / 1e12, "unit": "TFLOP/s",
+                    "sample": f"{fdone} heads, forward only, {fdt:.2f} s", "seconds": fdt},
+            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
 
 
 def bench_softmax(args):
@@ -267,7 +289,7 @@ def bench_softmax(args):
         result["cpu_baseline"] = {"value": 8.0 * done * cols / dt / 1e9, "unit": "GB/s",
                                   "cores": int(threads), "kind": "oracle",
                                   "sample": f"{done} of {rows} rows, fp64 NumPy, {dt:.2f} s",
-                                  "seconds": dt}
+                                  "seconds": dt, "cpu": cpu_model(), "host_cpus": os.cpu_count()}
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
@@ -357,7 +379,7 @@ def bench_decode(args):
         result["cpu_baseline"] = {"value": per_head * done / dt / 1e9, "unit": "GB/s",
                                   "cores": int(threads), "kind": "oracle",
                                   "sample": f"{done} of {B * H} heads, fp64 NumPy, {dt:.2f} s",
-                                  "seconds": dt}
+                                  "seconds": dt, "cpu": cpu_model(), "host_cpus": os.cpu_count()}
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
@@ -666,8 +688,13 @@ def main():
     wall = time.perf_counter() - t0
     print(f"[bench] timed {K} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
-    per = {name: float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(K)]))
-           for j, (name, _) in enumerate(stages)}
+    times = {name: np.array([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(K)])
+             for j, (name, _) in enumerate(stages)}
+    per = {name: float(t.mean()) for name, t in times.items()}
+    spread = {name: {"mean": round(float(t.mean()), 4), "median": round(float(np.median(t)), 4),
+                     "p10": round(float(np.percentile(t, 10)), 4),
+                     "p90": round(float(np.percentile(t, 90)), 4)}
+              for name, t in times.items()}
     fwd_ms = per["fa_fwd_kernel"]
     bwd_ms = sum(per[n] for n, _ in stages[1:])
     rho = kept_fraction(w.N, w.causal, bm)
@@ -719,6 +746,7 @@ def main():
         "fwd_bwd": {"ms": round(fb_ms, 4), "tflops": round(fb_tf, 2),
                     "frac_of_peak": round(fb_tf / PEAK_BF16_TFLOPS, 4)},
         "kernel_ms": {n: round(t, 4) for n, t in per.items()},
+        "kernel_ms_spread": spread,
         "roofline": roofline,
         "io_bytes": {k: (int(v) if k != "rows_per_workgroup_fwd" else v) for k, v in io.items()},
         "device": device_info(lib, dev.index or 0),
