@@ -21,7 +21,7 @@ MASK_BLOCK_SIZE = 128
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess", "fa_bwd_dkdv",
            "fa_bwd_dq", "fa_decode_workspace_size", "fa_decode", "fa_fwd_kv_outer_workspace_size",
-           "fa_fwd_kv_outer", "fa_softmax_rows", "fa_strerror")
+           "fa_fwd_kv_outer", "fa_softmax_rows", "fa_bwd_noalloc", "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -52,6 +52,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp,
                            sz, vp]
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                   mp, vp]
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, sz, vp]
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz, vp]
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, mp, vp, sz, vp]

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_softmax.hip",
-           "fa_decode.hip", "fa_fwd_kv_outer.hip"]
+           "fa_decode.hip", "fa_fwd_kv_outer.hip", "fa_noalloc.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: packed FP32 VALU instructions are kept out of the code.

@@ -194,6 +194,8 @@ const char* fa_strerror(int status) {
     case FA_ERR_HIP: return "HIP runtime error at kernel launch";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIAS: return "an output buffer overlaps another argument buffer";
+    case FA_ERR_SCRATCH:
+      return "too large for fa_bwd_noalloc's fixed 16 MiB scratch (B*H*ceil(N/128)*128 > 2^21)";
     default: return "unknown status";
   }
 }

@@ -22,7 +22,8 @@
  *              d fastest. lse is [B, H, N] float32 (natural-log logsumexp of the
  *              scaled, masked scores of each query row).
  *   Memory     every data pointer is a DEVICE pointer owned by the caller; the
- *              library allocates nothing and keeps no mutable global state.
+ *              library allocates nothing; its only global state is the
+ *              fixed device array of fa_bwd_noalloc (and its cached address).
  *              Inputs are read-only; outputs must not overlap any input.
  *   Alignment  data pointers must be 16-byte aligned.
  *   Limits     B, H, N >= 0 (a zero extent is a no-op that returns FA_OK);
@@ -58,7 +59,8 @@ typedef enum fa_status {
   FA_ERR_WORKSPACE = -5, /* backward workspace missing or too small                */
   FA_ERR_HIP = -6,       /* the HIP runtime reported an error at launch            */
   FA_ERR_SCALE = -7,     /* scale is not finite and > 0                            */
-  FA_ERR_ALIAS = -8      /* an output range overlaps an input range                */
+  FA_ERR_ALIAS = -8,     /* an output range overlaps an input range                */
+  FA_ERR_SCRATCH = -9    /* problem too large for fa_bwd_noalloc's fixed scratch   */
 } fa_status;
 
 /* Mask kinds (bit flags; 0 = every key visible to every query). */
@@ -211,6 +213,23 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
  * Asynchronous on `stream` like every entry point.
  */
 int fa_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream);
+
+/*
+ * fa_bwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, results and kernels as fa_bwd, without the workspace: the per-row
+ * workspace lives in a fixed 16 MiB device array of the library (one copy per
+ * GPU, kept until the process ends), so B * H * ceil(N / 128) * 128 must be at
+ * most 2^21 rows, else FA_ERR_SCRATCH before anything is enqueued. The call
+ * itself allocates nothing (its first call on a device looks the array's
+ * address up once). Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (several streams or host threads) race and must be
+ * serialised by the caller. The array needs no initialisation between calls.
+ * The GPU is the one `stream` belongs to (the current device for NULL).
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, const fa_mask_t* mask, void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* fa_strerror(int status);

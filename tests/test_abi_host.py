@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 LIB = os.path.join(ROOT, "exact_io_aware_61_amd", "libfa.so")
 
-OK, NULL, SHAPE, MASK, ALIGN, WS, HIP, SCALE, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, SHAPE, MASK, ALIGN, WS, HIP, SCALE, ALIAS, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 
 @pytest.fixture(scope="module")
@@ -36,7 +36,7 @@ def test_header_declares_the_abi():
     assert names == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
                             "fa_bwd_dkdv", "fa_bwd_dq", "fa_decode_workspace_size", "fa_decode",
                             "fa_fwd_kv_outer_workspace_size", "fa_fwd_kv_outer",
-                            "fa_softmax_rows", "fa_strerror"])
+                            "fa_softmax_rows", "fa_bwd_noalloc", "fa_strerror"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_strerror_covers_every_status(lib):
     msgs = {s: lib.fa_strerror(s).decode() for s in (OK, NULL, SHAPE, MASK, ALIGN, WS, HIP, SCALE,
-                                                     ALIAS)}
+                                                     ALIAS, SCRATCH)}
     assert len(set(msgs.values())) == len(msgs)
     assert lib.fa_strerror(12345).decode() == "unknown status"
 

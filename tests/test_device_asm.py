@@ -18,7 +18,7 @@ import pytest
 
 from exact_io_aware_61_amd import build as fab
 
-SOURCES = [s for s in fab.SOURCES if s != "fa_api.hip"]
+SOURCES = [s for s in fab.SOURCES if s not in ("fa_api.hip", "fa_noalloc.hip")]   # kernels only
 
 
 @pytest.fixture(scope="module")
