@@ -17,11 +17,14 @@
 // N, and rows with no visible key (LSE = -inf), get L2 = +inf and D = 0: their
 // probabilities recompute to exactly 0 with no test in the kernels.
 //
-// dK/dV kernel, per workgroup of 4 waves = 128 keys; wave w owns keys
-// key0 + 32w .. +31, keeps their K and V rows in VGPRs and their dK^T, dV^T
-// accumulators on chip. Per block of 64 query rows (the Q and dO tiles and the
-// rows' L2 and D reach LDS by direct global->LDS loads, 2-3 blocks ahead),
-// per wave and 32-row sub-tile:
+// Two dK/dV kernels share the arithmetic below and differ in where K and V sit.
+// At d = 64 (fa_bwd_dkdv_kernel), a workgroup of 4 waves = 128 keys; wave w
+// owns keys key0 + 32w .. +31, keeps their K and V rows in VGPRs and their
+// dK^T, dV^T accumulators on chip; two workgroups share a CU. At d = 128
+// (fa_bwd_dkdv8_kernel, further down) those registers would leave room for one
+// wave per SIMD only, so K and V are read from LDS and 8 waves split the work
+// (two per SIMD). Per block of 64 query rows (the Q and dO tiles and the rows'
+// L2 and D reach LDS by direct global->LDS loads), per wave and 32-row sub-tile:
 //   S  = Q K_w^T, dP = dO V_w^T   MFMA 32x32x16, Q/dO rows by 16-byte LDS reads;
 //                                 each lane holds one key column.
 //   P  = 2^(S scale log2e - L2_i), dS = P o (dP - D_i)
@@ -97,10 +100,9 @@ struct BwdCfg {
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BN = 32 * WAVES;           // keys per workgroup (= block-mask granularity)
-  // Query rows per block. 64 at both head dims: at d=64 that keeps the
-  // four-stage ring at 68 KiB, so two workgroups share a CU and each SIMD runs
-  // two waves (one wave's softmax under the other's products); at d=128 the
-  // registers allow one wave per SIMD whatever the ring.
+  // Query rows per block: 64 keeps the four-stage ring at 68 KiB at d=64, so
+  // two workgroups share a CU and each SIMD runs two waves (one wave's softmax
+  // under the other's products).
   static constexpr int BM = 64;
   static constexpr int IT = BM / 32;              // 32-row sub-tiles
   static constexpr int KS = D / 16;               // 16-column MFMA k-steps over the head dim
@@ -136,9 +138,11 @@ struct BwdParams {
   int nb;
 };
 
+// dK/dV kernel at d = 64 (fa_bwd_dkdv8_kernel below serves d = 128).
 template <int D, bool CAUSAL, bool BLOCK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
+  static_assert(D == 64, "d = 128 runs fa_bwd_dkdv8_kernel");
   using C = BwdCfg<D>;
   // [stage][Q tile, dO tile, L2 rows, D rows]
   __shared__ __attribute__((aligned(16))) bf16 smem[C::NSTAGE * C::STAGE];
@@ -278,9 +282,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // Software pipeline over 32-row sub-tiles. At d=128 there is one wave per
-  // SIMD, so the wave's own instruction order decides what overlaps (at d=64 a
-  // second workgroup's wave shares the SIMD). At the start of a sub-tile
+  // Software pipeline over 32-row sub-tiles (a second workgroup's wave shares
+  // each SIMD and fills in while this one waits). At the start of a sub-tile
   // its Q/dO row operands are already in registers (read during the previous
   // sub-tile's dV/dK products); its transposed operands and row statistics
   // are read between its S/dP products, two reads per product; after the
@@ -490,6 +493,318 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// dK/dV kernel at d = 128 with two waves per SIMD.
+//
+// A wave that keeps 32 keys' K and V rows and their fp32 dK/dV accumulators in
+// registers needs more than half the register file at d = 128, so only one such
+// wave fits per SIMD and every stall of its in-order instruction stream (the
+// softmax, the burst of global->LDS loads at a block boundary, waits on LDS)
+// leaves the matrix unit idle. Here the workgroup's K and V tiles (128 keys)
+// sit in LDS instead, read as MFMA operands like the Q and dO rows, and the
+// workgroup has 8 waves: wave w owns keys 32 (w mod 4) .. +31 for the 32-row
+// sub-tile w / 4 of every 64-row block, so each key group has two waves, each
+// summing half of the row sub-tiles into its own accumulators. The two halves
+// are added through LDS at the end, in a fixed order (bitwise reproducible).
+// Q/dO tiles and row statistics arrive by direct global->LDS loads into a
+// two-stage ring (one block ahead).
+struct Dkdv8Cfg {
+  static constexpr int D = 128;
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BN = 128;                  // keys per workgroup
+  static constexpr int BM = 64;                   // query rows per block
+  static constexpr int KS = D / 16;
+  static constexpr int CT = D / 32;
+  static constexpr int C = D / 8;                 // 16-byte chunks per row
+  static constexpr int KVROW = D + 8;             // K/V tile row pitch (elements): 272 bytes
+  static constexpr int KVT = BN * KVROW;          // elements of the K or V tile
+  static constexpr int TILE = BM * D;             // elements of a Q or dO tile
+  static constexpr int STAGE = 2 * TILE + 2 * BM * 2;   // + L2 and D rows (floats)
+  static constexpr int NSTAGE = 2;
+  static constexpr int SLOTS = TILE / 512;        // 1 KiB slots per Q/dO tile
+  static constexpr int LOADERS = 4;              // waves 4..7 issue the ring's loads
+  static constexpr int SPW = SLOTS / LOADERS;
+  static constexpr int KVCH = BN * C / THREADS;   // 16-byte K (and V) chunks per thread
+  static_assert(SLOTS % LOADERS == 0 && (BN * C) % THREADS == 0, "loads split evenly");
+  static_assert(kBwdRowPad % BM == 0, "row padding covers whole row blocks");
+};
+
+template <bool CAUSAL, bool BLOCK>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkdv8_kernel(BwdParams p) {
+  using C = Dkdv8Cfg;
+  constexpr int D = C::D;
+  // [K tile][V tile][stage 0][stage 1]; a stage is [Q tile, dO tile, L2 rows, D rows]
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::KVT + C::NSTAGE * C::STAGE];
+  __shared__ uint32_t mbits[BLOCK ? kMaskWords : 1];
+  static_assert((2 * C::KVT + C::NSTAGE * C::STAGE) * 2 + (BLOCK ? kMaskWords * 4 : 4) <=
+                    160 * 1024,
+                "LDS budget");
+  static_assert(2 * C::KVT + C::NSTAGE * C::STAGE >= 4 * 64 * 128 * 2,
+                "the accumulator exchange fits in the tile area");
+  static_assert((C::KVROW * 2) % 16 == 0, "16-byte aligned K/V rows");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kq = wave & 3;     // key group: keys 32 kq .. +31 of the block
+  const int par = wave >> 2;   // row sub-tile of every block this wave takes
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int g16 = lane >> 4;
+  const int i16 = lane & 15;
+
+  const WgCoord wc = wg_coord<BLOCK>(blockIdx.x, p.BH, (p.N + C::BN - 1) / C::BN);
+  const int bh = wc.bh;
+  const int kb = wc.blk;
+  const int N = p.N;
+  const int64_t head = (int64_t)bh * N * D;
+  const bf16* __restrict__ Qh = p.q + head;
+  const bf16* __restrict__ Kh = p.k + head;
+  const bf16* __restrict__ Vh = p.v + head;
+  const bf16* __restrict__ dOh = p.dout + head;
+  const float* __restrict__ L2h = p.l2 + (int64_t)bh * p.Np;
+  const float* __restrict__ Dh = p.dvec + (int64_t)bh * p.Np;
+
+  const int key0 = kb * C::BN;
+  const int mykey = key0 + 32 * kq + l32;
+
+  if (BLOCK) {
+    const int nw = (p.nb + 63) / 64;
+    const uint8_t* grid = p.blocks + bh * p.blocks_bh_stride;
+    for (int j = wave; j < nw; j += C::WAVES) {
+      const int b = j * 64 + lane;
+      const bool keep = b < p.nb && grid[(int64_t)b * p.nb + kb] != 0;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+      if (lane == 0) {
+        mbits[2 * j] = (uint32_t)bal;
+        mbits[2 * j + 1] = (uint32_t)(bal >> 32);
+      }
+    }
+  }
+
+  if (BLOCK) __syncthreads();   // the mask bits, before any wave reads them
+  bf16* const Ks = smem;
+  bf16* const Vs = smem + C::KVT;
+  bf16* const ring = smem + 2 * C::KVT;
+
+  // K and V tiles of the block's 128 keys (keys past N clamped; masked below),
+  // loaded once through registers into rows padded to 272 bytes: the rows of a
+  // 16-byte operand read then start 4 banks apart, which keeps the reads free
+  // of bank conflicts with one base address and immediate offsets per lane
+  // (the swizzle the direct loads need would cost a register per k-step).
+#pragma unroll
+  for (int i = 0; i < C::KVCH; ++i) {
+    const int idx = tid + i * C::THREADS;
+    const int r = idx / C::C, ch = idx % C::C;
+    const int64_t src = (int64_t)min(key0 + r, N - 1) * D + 8 * ch;
+    *reinterpret_cast<bf16x8*>(Ks + r * C::KVROW + 8 * ch) =
+        *reinterpret_cast<const bf16x8*>(Kh + src);
+    *reinterpret_cast<bf16x8*>(Vs + r * C::KVROW + 8 * ch) =
+        *reinterpret_cast<const bf16x8*>(Vh + src);
+  }
+
+  // Lane offsets: B operands (this lane's key row of K and V), A operands (rows
+  // of the wave's Q/dO sub-tile), transposing reads of the same sub-tile.
+  const int kbase = (32 * kq + l32) * C::KVROW + 8 * hh;
+  int qoff[C::KS], troff[C::CT][2];
+#pragma unroll
+  for (int kk = 0; kk < C::KS; ++kk) qoff[kk] = toff<C::C>(32 * par + l32, 16 * kk + 8 * hh);
+#pragma unroll
+  for (int ct = 0; ct < C::CT; ++ct) {
+    const int n0 = 32 * ct + 16 * (g16 & 1) + 4 * (i16 & 3);
+    troff[ct][0] = toff<C::C>(32 * par + 4 * hh + (i16 >> 2), n0);
+    troff[ct][1] = toff<C::C>(32 * par + 8 + 4 * hh + (i16 >> 2), n0);
+  }
+
+  f32x16 dk[C::CT], dv[C::CT];
+#pragma unroll
+  for (int ct = 0; ct < C::CT; ++ct) {
+    dk[ct] = f32x16{};
+    dv[ct] = f32x16{};
+  }
+
+  const int n_rb = (N + C::BM - 1) / C::BM;
+  const int rb_begin = CAUSAL ? key0 / C::BM : 0;
+  auto kept = [&](int rb) -> bool {
+    if (!BLOCK) return true;
+    const int b = (rb * C::BM) / 128;
+    return (mbits[b >> 5] >> (b & 31)) & 1u;
+  };
+  auto next_kept = [&](int rb) -> int {
+    ++rb;
+    while (rb < n_rb && !kept(rb)) ++rb;
+    return rb;
+  };
+
+  // Only the waves of the second row sub-tile (4..7) issue the ring's loads:
+  // while they wait on the load path after a barrier, the waves of the first
+  // sub-tile on the same SIMDs already compute, so the two waves of a SIMD
+  // leave the barrier a phase apart.
+  const bool loader = __builtin_amdgcn_readfirstlane(wave) >= 4;   // uniform branch
+  const int lw = wave - 4;
+  const bool row_loader = lw == 0 || lw == 1;   // waves 4 and 5 load the L2 and D rows
+  const int uwave = __builtin_amdgcn_readfirstlane(lw);
+  const uint32_t ring0 = lds_byte_addr(ring);
+  uint32_t soff[C::SPW];
+#pragma unroll
+  for (int i = 0; i < C::SPW; ++i) soff[i] = slot_offset<C::C>(lw + i * C::LOADERS, lane, 2 * D);
+  auto issue = [&](int rb, int stage) {
+    if (!loader) return;
+    const int row0 = rb * C::BM;
+    bf16* Qs = ring + stage * C::STAGE;
+    bf16* dOs = Qs + C::TILE;
+    float* Rs = reinterpret_cast<float*>(dOs + C::TILE);
+    if (row0 + C::BM <= N) {
+      const bf16* qb = Qh + (int64_t)row0 * D;
+      const bf16* gb = dOh + (int64_t)row0 * D;
+      const uint32_t qdst = ring0 + 2u * (uint32_t)(stage * C::STAGE);
+#pragma unroll
+      for (int i = 0; i < C::SPW; ++i) {
+        const uint32_t o = 2u * 512u * (uint32_t)(uwave + i * C::LOADERS);
+        dma16_s(soff[i], qb, qdst + o);
+        dma16_s(soff[i], gb, qdst + 2u * C::TILE + o);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::SPW; ++i) {
+        const int slot = lw + i * C::LOADERS;
+        dma_slot<C::C>(Qs, slot, lane,
+                       [&](int r) { return Qh + (int64_t)min(row0 + r, N - 1) * D; });
+        dma_slot<C::C>(dOs, slot, lane,
+                       [&](int r) { return dOh + (int64_t)min(row0 + r, N - 1) * D; });
+      }
+    }
+    if (row_loader) {
+      const float* src = (lw == 0 ? L2h : Dh) + row0 + lane;
+      dma4(src, Rs + lw * C::BM);
+    }
+  };
+
+  // Double-buffered ring: at the top of block j every thread waits for all its
+  // loads (block j's; block j+1 is not issued yet), the barrier publishes them
+  // and guarantees every wave has finished block j-1, whose stage the loads of
+  // block j+1 then take while block j is computed.
+  int rb = rb_begin;
+  if (rb < n_rb && !kept(rb)) rb = next_kept(rb);
+  if (rb < n_rb) issue(rb, 0);
+  int stage = 0;
+
+  auto block = [&](auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const int nxt = next_kept(rb);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (nxt < n_rb) issue(nxt, stage ^ 1);
+    const bf16* Qs = ring + stage * C::STAGE;
+    const bf16* dOs = Qs + C::TILE;
+    const float* Ls = reinterpret_cast<const float*>(dOs + C::TILE);
+    const float* Ds = Ls + C::BM;
+    const int row0 = rb * C::BM + 32 * par;   // the wave's sub-tile
+    // S = Q K^T and dP = dO V^T for the wave's 32 rows x 32 keys.
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk) {
+      s = mfma32(lds_b128(Qs + qoff[kk]), lds_b128(Ks + kbase + 16 * kk), s);
+      dp = mfma32(lds_b128(dOs + qoff[kk]), lds_b128(Vs + kbase + 16 * kk), dp);
+    }
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int rl = 32 * par + 8 * g + 4 * hh;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + rl);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + rl);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = 4 * g + r;
+        float pe = fast_exp2(__builtin_fmaf(s[v], p.sl2, -l4[r]));
+        if (EDGE) {
+          const int row = row0 + 8 * g + 4 * hh + r;
+          if ((CAUSAL && mykey > row) || mykey >= N) pe = 0.f;
+        }
+        pv[v] = pe;
+        dsv[v] = pe * (dp[v] - d4[r]);
+      }
+    }
+    bf16x8 pk[2], dsk[2];
+    pk[0] = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+    pk[1] = to_bf16x8(pv[8], pv[9], pv[10], pv[11], pv[12], pv[13], pv[14], pv[15]);
+    dsk[0] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+    dsk[1] = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ro = 16 * h * D;
+        const bf16x8 ota = cat(lds_tr(dOs + troff[ct][0] + ro), lds_tr(dOs + troff[ct][1] + ro));
+        const bf16x8 qta = cat(lds_tr(Qs + troff[ct][0] + ro), lds_tr(Qs + troff[ct][1] + ro));
+        dv[ct] = mfma32(ota, pk[h], dv[ct]);
+        dk[ct] = mfma32(qta, dsk[h], dk[ct]);
+      }
+    }
+    stage ^= 1;
+    rb = nxt;
+  };
+  auto edge_block = [&](int b) {
+    return (CAUSAL && b * C::BM < key0 + C::BN - 1) || key0 + C::BN > N;
+  };
+  // The first block's barrier also publishes the K/V tiles.
+  while (rb < n_rb && edge_block(rb)) block(std::true_type{});
+  while (rb < n_rb) block(std::false_type{});
+
+  // Sum the two waves' halves of each key group: waves 4..7 hand their
+  // accumulators over through LDS (the tile area, free once every wave is past
+  // its last block), waves 0..3 add them to their own and write dK, dV.
+  wait_vmcnt<0>();
+  __syncthreads();
+  float* xch = reinterpret_cast<float*>(smem) + (size_t)kq * 64 * 128;
+  if (par == 1) {
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        *reinterpret_cast<f32x4*>(xch + ((2 * ct) * 4 + q4) * 256 + lane * 4) =
+            f32x4{dk[ct][4 * q4], dk[ct][4 * q4 + 1], dk[ct][4 * q4 + 2], dk[ct][4 * q4 + 3]};
+        *reinterpret_cast<f32x4*>(xch + ((2 * ct + 1) * 4 + q4) * 256 + lane * 4) =
+            f32x4{dv[ct][4 * q4], dv[ct][4 * q4 + 1], dv[ct][4 * q4 + 2], dv[ct][4 * q4 + 3]};
+      }
+    }
+  }
+  __syncthreads();
+  if (par == 0) {
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(xch + ((2 * ct) * 4 + q4) * 256 + lane * 4);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(xch + ((2 * ct + 1) * 4 + q4) * 256 + lane * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dk[ct][4 * q4 + e] += a[e];
+          dv[ct][4 * q4 + e] += b[e];
+        }
+      }
+    }
+    if (mykey < N) {
+      bf16* dkrow = p.dk + head + (int64_t)mykey * D;
+      bf16* dvrow = p.dv + head + (int64_t)mykey * D;
+#pragma unroll
+      for (int ct = 0; ct < C::CT; ++ct) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = 32 * ct + 8 * g + 4 * hh;
+          *reinterpret_cast<bf16x4*>(dkrow + c) =
+              to_bf16x4(dk[ct][4 * g] * p.scale, dk[ct][4 * g + 1] * p.scale,
+                        dk[ct][4 * g + 2] * p.scale, dk[ct][4 * g + 3] * p.scale);
+          *reinterpret_cast<bf16x4*>(dvrow + c) =
+              to_bf16x4(dv[ct][4 * g], dv[ct][4 * g + 1], dv[ct][4 * g + 2], dv[ct][4 * g + 3]);
+        }
+      }
+    }
+  }
+}
+
 template <int D, bool CAUSAL, bool BLOCK>
 hipError_t launch_dkdv_one(const BwdArgs& a, hipStream_t stream) {
   using C = BwdCfg<D>;
@@ -512,8 +827,12 @@ hipError_t launch_dkdv_one(const BwdArgs& a, hipStream_t stream) {
   p.nb = a.mask.nb;
   const int n_kb = (a.N + C::BN - 1) / C::BN;
   const dim3 grid((unsigned)n_kb * (unsigned)a.BH);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, BLOCK>), grid, dim3(C::THREADS), 0, stream,
-                     p);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((fa_bwd_dkdv8_kernel<CAUSAL, BLOCK>), grid, dim3(Dkdv8Cfg::THREADS), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, BLOCK>), grid, dim3(C::THREADS), 0, stream,
+                       p);
   return hipGetLastError();
 }
 
