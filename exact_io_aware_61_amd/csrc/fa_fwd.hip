@@ -41,8 +41,11 @@ namespace {
 template <int D, bool BLOCK>
 struct FwdCfg {
   // A block mask works on 128-row blocks: masked launches use 128-row
-  // workgroups so that every wave of a workgroup keeps the same tiles.
-  static constexpr int WAVES = BLOCK ? 4 : 8;
+  // workgroups so that every wave of a workgroup keeps the same tiles. At d=64
+  // every launch does, with a two-stage ring: the kernel then fits in 128
+  // registers and 32 KiB, so four workgroups share a CU (four waves per SIMD)
+  // and each tile barrier waits for four waves instead of eight.
+  static constexpr int WAVES = (BLOCK || D == 64) ? 4 : 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;           // query rows per workgroup
   static constexpr int BN = 64;                   // keys per K/V tile
@@ -52,9 +55,10 @@ struct FwdCfg {
   static constexpr int CT = D / 32;               // 32-column sub-tiles of O^T
   static constexpr int TILE = BN * D;             // elements per K or V tile (swizzled, unpadded)
   static constexpr int STAGE = 2 * TILE;          // K tile, V tile
-  // Tiles in flight (three: two loading while one is used; two where LDS
-  // must hold two workgroups per CU).
-  static constexpr int NSTAGE = (BLOCK && D == 128) ? 2 : 3;
+  // Tiles in flight: three (two loading while one is used) for the 8-wave
+  // workgroups; two for the 4-wave ones, whose LDS must hold several
+  // workgroups per CU.
+  static constexpr int NSTAGE = (BLOCK || D == 64) ? 2 : 3;
   static constexpr int SLOTS = BN * C / 64;       // 1 KiB direct-load slots per tile
   static constexpr int SPW = SLOTS / WAVES;       // ... per wave
   static constexpr int LPT = 2 * SPW;             // direct loads per thread per K+V tile
