@@ -385,6 +385,11 @@ def bench_decode(args):
     print(json.dumps(result), flush=True)
 
 
+def fwd_rows_per_workgroup(d: int, masked: bool) -> int:
+    """Query rows per fa_fwd workgroup: 256 at d=128 without a block mask, else 128."""
+    return 128 if (masked or d == 64) else 256
+
+
 def kv_outer_io_model(N: int, d: int, causal: bool, heads: int) -> float:
     """Device bytes of the K/V-outer forward per launch, counted from its loops.
 
@@ -460,7 +465,7 @@ def bench_kv_outer(args):
     flop = 4.0 * w.B * w.H * w.N * w.N * w.d * rho
     heads = w.B * w.H
     model_kvo = kv_outer_io_model(w.N, w.d, w.causal, heads)
-    br = 256
+    br = fwd_rows_per_workgroup(w.d, False)
     model_fwd = heads * (4 * w.N * w.d + 4 * w.N * w.d * (-(-w.N // br)) * rho + 4 * w.N)
     result = {
         "metric": "forward TFLOP/s, K/V-outer loop order", "value": round(flop / t_kvo / 1e9, 2),
@@ -563,7 +568,7 @@ def bench_naive(args):
     rho = kept_fraction(w.N, w.causal, bm)
     flop = 4.0 * w.B * w.H * w.N * w.N * w.d * rho
     heads = w.B * w.H
-    br = 128 if bm is not None else 256
+    br = fwd_rows_per_workgroup(w.d, bm is not None)
     io = naive_io_model(w.N, w.d, drop is not None, heads)
     io["fa_fwd_compulsory"] = float(heads * (8 * w.N * w.d + 4 * w.N))
     io["fa_fwd_tile_model"] = float(heads * (4 * w.N * w.d + 4 * w.N * w.d * (-(-w.N // br)) * rho
@@ -723,7 +728,7 @@ def main():
     # forward, where every block of BR query rows re-reads the K and V tiles it
     # attends (4*N*d*ceil(N/BR)*rho per head: the Theta(N^2 d^2 / M) term) on top
     # of reading Q and writing O once. BR is the forward's rows per workgroup.
-    br = 128 if bm is not None else 256
+    br = fwd_rows_per_workgroup(w.d, bm is not None)
     heads = w.B * w.H
     io = {"compulsory_fwd": heads * (8 * w.N * w.d + 4 * w.N),
           "tile_model_fwd": heads * (4 * w.N * w.d + 4 * w.N * w.d * (-(-w.N // br)) * rho

@@ -463,12 +463,16 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   auto edge_block = [&](int b) {
     return (CAUSAL && b * C::BM < key0 + C::BN - 1) || key0 + C::BN > N;
   };
+  // Two workgroups share a CU: keep them at one pace.
+  int prio_set = -1;
   while (rb < n_rb && edge_block(rb)) {
+    prio_by_progress(rb - rb_begin, n_rb - rb_begin, prio_set);
     const int nxt = r1;
     block(std::true_type{});
     rb = nxt;
   }
   while (rb < n_rb) {
+    prio_by_progress(rb - rb_begin, n_rb - rb_begin, prio_set);
     const int nxt = r1;
     block(std::false_type{});
     rb = nxt;

@@ -275,8 +275,12 @@ void fa_bwd_dq_kernel(DqParams p) {
   wait_vmcnt<0>();
   if (C::NSTAGE == 3 && kn < kt_end) issue(kn, 1);
   int stage = 0;
+  // At d=64 three workgroups share a CU: keep them at one pace.
+  const int kt_first = kt;
+  int prio_set = -1;
   while (kt < kt_end) {
     const int knn = kn < kt_end ? next_kept(kn) : kt_end;
+    if (D == 64) prio_by_progress(kt - kt_first, kt_end - kt_first, prio_set);
     if (C::NSTAGE == 3 && kn < kt_end)
       wait_vmcnt<C::LPT>();
     else

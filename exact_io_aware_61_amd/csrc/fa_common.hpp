@@ -158,6 +158,27 @@ __device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32
                : "memory", "m0");
 }
 
+// Issue priority from progress through a sweep: 3 for its first quarter down
+// to 0 for its last. Where several workgroups share a CU the arbiter otherwise
+// favours the oldest waves, so the workgroups of one CU finish one after
+// another and the CU ends each round with fewer and fewer of them resident;
+// with this, a workgroup that is behind gets the issue slots and the CU's
+// workgroups advance at one pace.
+__device__ __forceinline__ void prio_by_progress(int done, int total, int& cur) {
+  const int q = __builtin_amdgcn_readfirstlane(min(3, (4 * done) / max(total, 1)));
+  if (q != cur) {
+    cur = q;
+    if (q == 0)
+      __builtin_amdgcn_s_setprio(3);
+    else if (q == 1)
+      __builtin_amdgcn_s_setprio(2);
+    else if (q == 2)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
+  }
+}
+
 // LDS byte address of a __shared__ location (for dma16_s).
 __device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
