@@ -37,18 +37,22 @@ struct DqCfg {
   // workgroups so that every wave of a workgroup keeps the same tiles. At d=64
   // every launch does: the kernel fits in 168 registers and a 48 KiB ring, so
   // three 4-wave workgroups share a CU (three waves per SIMD), where 8-wave
-  // workgroups would leave it at two.
+  // workgroups would leave it at two. Unmasked at d=64 the tiles are 32 keys
+  // in a two-stage ring, which brings the kernel to 128 registers: four
+  // workgroups and four waves per SIMD. (With a block mask the sweeps are short
+  // and the per-tile costs of 32-key tiles outweigh the occupancy.)
+  static constexpr bool SMALL = D == 64 && !BLOCK;
   static constexpr int WAVES = (BLOCK || D == 64) ? 4 : 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;           // query rows per workgroup
-  static constexpr int BN = 64;                   // keys per K/V tile
+  static constexpr int BN = SMALL ? 32 : 64;      // keys per K/V tile
   static constexpr int C = D / 8;                 // 16-byte chunks per tile row
   static constexpr int KS = D / 16;
   static constexpr int NT = BN / 32;
   static constexpr int CT = D / 32;
   static constexpr int TILE = BN * D;             // elements per K or V tile (swizzled, unpadded)
   static constexpr int STAGE = 2 * TILE;
-  static constexpr int NSTAGE = (BLOCK && D == 128) ? 2 : 3;
+  static constexpr int NSTAGE = (SMALL || (BLOCK && D == 128)) ? 2 : 3;
   static constexpr int SLOTS = BN * C / 64;
   static constexpr int SPW = SLOTS / WAVES;
   static constexpr int LPT = 2 * SPW;
@@ -76,7 +80,8 @@ struct DqParams {
 };
 
 template <int D, bool CAUSAL, bool BLOCK>
-__global__ __launch_bounds__((DqCfg<D, BLOCK>::THREADS)) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__((DqCfg<D, BLOCK>::THREADS))
+__attribute__((amdgpu_waves_per_eu(DqCfg<D, BLOCK>::SMALL ? 4 : 2)))
 void fa_bwd_dq_kernel(DqParams p) {
   using C = DqCfg<D, BLOCK>;
   __shared__ __attribute__((aligned(16))) bf16 smem[C::NSTAGE * C::STAGE];  // [stage][K, V]
