@@ -194,24 +194,51 @@ void fa_decode_split_kernel(DecParams p) {
   }
 }
 
-// Merge of the chunks: one workgroup of D threads per (b, h, query row).
+// Merge of the chunks: one workgroup of D threads per (b, h, query row), one
+// output column per thread. One pass over the chunks with the online-softmax
+// merge (the running max M moves to the larger of M and the chunks' maxima,
+// rescaling the sums by 2^(M_old - M_new)), reading eight chunks' partial
+// states per step so that their loads are in flight together.
 template <int D>
 __global__ __launch_bounds__(D) void fa_decode_combine_kernel(const float* part_o,
                                                              const float* part_ml, bf16* o,
                                                              float* lse, int nsplit, int Nq) {
+  constexpr int U = 8;
   const int row = blockIdx.x;             // (bh, q) flattened
   const int bh = row / Nq, q = row % Nq;
   const int c = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[2 * (((int64_t)bh * nsplit + s) * Nq + q)]);
-  float L = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const int64_t base = ((int64_t)bh * nsplit + s) * Nq + q;
-      const float w = fast_exp2(part_ml[2 * base] - M);   // 0 for a chunk that saw nothing
-      L += w * part_ml[2 * base + 1];
-      acc += w * part_o[base * D + c];
+  const int64_t first = (int64_t)bh * nsplit * Nq + q;   // chunk s sits at first + s * Nq
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  auto merge = [&](const float* mm, const float* ll, const float* oo, int n) {
+    float mx = M;
+    for (int j = 0; j < n; ++j) mx = fmaxf(mx, mm[j]);
+    if (mx == -INFINITY) return;            // nothing visible in any chunk so far
+    const float a = M == -INFINITY ? 0.f : fast_exp2(M - mx);
+    L *= a;
+    acc *= a;
+    for (int j = 0; j < n; ++j) {
+      const float w = fast_exp2(mm[j] - mx);   // 0 for a chunk that saw nothing
+      L += w * ll[j];
+      acc += w * oo[j];
     }
+    M = mx;
+  };
+  int s = 0;
+  for (; s + U <= nsplit; s += U) {
+    float mm[U], ll[U], oo[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t base = first + (int64_t)(s + j) * Nq;
+      mm[j] = part_ml[2 * base];
+      ll[j] = part_ml[2 * base + 1];
+      oo[j] = part_o[base * D + c];
+    }
+    merge(mm, ll, oo, U);
+  }
+  for (; s < nsplit; ++s) {
+    const int64_t base = first + (int64_t)s * Nq;
+    const float mm = part_ml[2 * base], ll = part_ml[2 * base + 1], oo = part_o[base * D + c];
+    merge(&mm, &ll, &oo, 1);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   o[(int64_t)row * D + c] = (bf16)(acc * inv);

@@ -66,10 +66,11 @@ struct DecodeArgs {
 };
 
 // Key split of the decoding kernels: nsplit chunks of `chunk` keys (a multiple
-// of 32) cover Nk. Enough waves to cover the chip several times over, chunks
-// of at least eight 32-key tiles.
+// of 32) cover Nk. About 1024 chunk waves in all (four per CU: measured faster
+// than 2048 to 8192 on every decode shape tried, the merge reading fewer
+// partial states), chunks of at least eight 32-key tiles.
 inline void decode_split(int BH, int Nk, int* nsplit, int* chunk) {
-  const int target = (2048 + BH - 1) / BH;
+  const int target = (1024 + BH - 1) / BH;
   const int max_split = Nk > 0 ? (Nk + 255) / 256 : 1;
   int ns = target < max_split ? target : max_split;
   if (ns < 1) ns = 1;
