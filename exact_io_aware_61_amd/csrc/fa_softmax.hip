@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void softmax_rows_reg(const float* x, float* y
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int i = lane + 64 * c;
-    v[c] = i < n4 ? xr[i] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    v[c] = i < n4 ? __builtin_nontemporal_load(&xr[i]) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   }
   float m = -INFINITY;
 #pragma unroll
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void softmax_rows_reg(const float* x, float* y
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int i = lane + 64 * c;
-    if (i < n4) yr[i] = v[c] * f;
+    if (i < n4) __builtin_nontemporal_store(v[c] * f, &yr[i]);
   }
 }
 
@@ -158,11 +158,11 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_rows_stream(const floa
     for (; i + 3 * kStreamThreads < n4; i += 4 * kStreamThreads) {
       f32x4 v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = x4[i + u * kStreamThreads];
+      for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(&x4[i + u * kStreamThreads]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) y4[i + u * kStreamThreads] = out(v[u]);
+      for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(out(v[u]), &y4[i + u * kStreamThreads]);
     }
-    for (; i < n4; i += kStreamThreads) y4[i] = out(x4[i]);
+    for (; i < n4; i += kStreamThreads) __builtin_nontemporal_store(out(__builtin_nontemporal_load(&x4[i])), &y4[i]);
   } else {
     for (int64_t i = tid; i < cols; i += kStreamThreads) yr[i] = exp_rel(xr[i], Mu) * inv;
   }
