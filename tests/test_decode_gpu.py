@@ -46,7 +46,9 @@ def _compare(o, lse, ref, heads=None):
 
 @pytest.mark.parametrize("B,H,Nq,Nk,d", [(1, 2, 1, 1, 64), (1, 2, 1, 37, 64), (2, 3, 4, 300, 128),
                                          (1, 2, 16, 1000, 128), (1, 1, 32, 2049, 64),
-                                         (2, 2, 8, 5, 128), (1, 3, 3, 0, 64)])
+                                         (2, 2, 8, 5, 128), (1, 3, 3, 0, 64),
+                                         # 20 key chunks: the merge's blocks of eight and a remainder
+                                         (1, 1, 4, 5000, 128)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_decode_parity(B, H, Nq, Nk, d, causal):
     q, k, v = _inputs(B, H, Nq, Nk, d, seed=500 + Nq * 7 + Nk)
