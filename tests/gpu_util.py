@@ -117,6 +117,15 @@ def errors(gpu: dict, ref: dict, heads=None):
     res = {}
     o_g, o_r = sel(to64(gpu["o"])), sel(ref["o"])
     res["o_maxabs"] = float(np.abs(o_g - o_r).max()) if o_r.size else 0.0
+    if o_r.size:
+        # The worst O entry, for the reading of the 1e-2 bar at large |O|: its
+        # reference magnitude, its error in bf16 units in the last place at that
+        # magnitude, and whether the GPU value is the correctly rounded reference.
+        i = int(np.argmax(np.abs(o_g - o_r)))
+        r, g = float(o_r.flat[i]), float(o_g.flat[i])
+        ulp = 2.0 ** (np.floor(np.log2(abs(r))) - 7) if r != 0 else 2.0 ** -133
+        rne = float(torch.tensor(r, dtype=torch.float64).to(torch.bfloat16).double())
+        res["o_worst"] = {"ref": r, "ulps": abs(g - r) / ulp, "correctly_rounded": g == rne}
     no = np.linalg.norm(o_r)
     res["o_relfro"] = float(np.linalg.norm(o_g - o_r) / no) if no > 0 else float(
         np.linalg.norm(o_g))

@@ -130,9 +130,15 @@ def test_rescale_parity(_lib, kind, d, N):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_rescale_late_outliers(_lib, d, causal):
-    """The last keys jump far above every earlier score: the maximum moves on the last tile."""
+    """The last keys jump far above every earlier score: the maximum moves on the last tile.
+
+    The outlier keys then dominate their rows, so O is close to a mean of a few V
+    rows; V is halved (exact in bf16) to keep |O| below 2, where one bf16 unit in
+    the last place stays under the 1e-2 O bar and the case measures the rescale
+    rather than the resolution of bf16 at |O| >= 2."""
     N = 600
     q, k, v, do = make_rising_scores(1, 2, N, d, 900 + d, late_outliers=5)
+    v = (v.float() * 0.5).to(torch.bfloat16)
     scale = float(np.float32(1 / math.sqrt(d)))
     ev = _events_all_heads(q, k, scale, causal, None)
     print(f"[case] late outliers d={d} causal={causal} events={ev}", flush=True)
