@@ -61,6 +61,8 @@ __global__ __launch_bounds__(256) void softmax_rows_reg(const float* x, float* y
   const f32x4* xr = reinterpret_cast<const f32x4*>(x + row * cols);
   f32x4* yr = reinterpret_cast<f32x4*>(y + row * cols);
   const int n4 = cols >> 2;
+  // Every element is read once and written once: non-temporal accesses keep
+  // the input and output streams from evicting each other in the L2.
   f32x4 v[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
@@ -154,6 +156,7 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_rows_stream(const floa
     auto out = [&](f32x4 v) {
       return f32x4{exp_rel(v[0], Mu), exp_rel(v[1], Mu), exp_rel(v[2], Mu), exp_rel(v[3], Mu)} * inv;
     };
+    // The row's last read and its only write: non-temporal (see softmax_rows_reg).
     int64_t i = tid;
     for (; i + 3 * kStreamThreads < n4; i += 4 * kStreamThreads) {
       f32x4 v[4];
