@@ -7,7 +7,9 @@
   as clobbered, and no compiler-generated code may hold a value in it across
   those statements);
 * no packed FP32 VALU instruction appears (the build turns the feature off);
-* no kernel spills registers or uses scratch memory.
+* no kernel spills registers or uses scratch memory;
+* the forward's workgroup shape matches the rows per workgroup that bench.py's
+  I/O model assumes.
 """
 import os
 import re
@@ -80,3 +82,28 @@ def test_no_spills_or_scratch(asm, src):
         if key == "sgpr_spill_count":
             continue   # SGPR spills go to VGPR lanes, not memory
         assert all(v == 0 for v in vals), f"{src}: {key} {list(zip(names, vals))}"
+
+
+def _kernel_entries(text):
+    """(name, max_flat_workgroup_size) of every kernel in the code-object metadata."""
+    out = []
+    for chunk in re.split(r"\n\s+- \.agpr_count:", text)[1:]:
+        name = re.search(r"^\s+\.name:\s+(\S+)", chunk, re.M)
+        size = re.search(r"^\s+\.max_flat_workgroup_size:\s+(\d+)", chunk, re.M)
+        if name and size:
+            out.append((name.group(1), int(size.group(1))))
+    return out
+
+
+def test_forward_rows_per_workgroup_match_bench_model(asm):
+    import bench
+    seen = 0
+    for name, threads in _kernel_entries(asm["fa_fwd.hip"]):
+        m = re.search(r"fa_fwd_kernelILi(\d+)ELb([01])ELb([01])E", name)
+        if not m:
+            continue
+        d, block = int(m.group(1)), m.group(3) == "1"
+        rows = threads // 64 * 32   # every wave owns 32 query rows
+        assert rows == bench.fwd_rows_per_workgroup(d, block), (name, threads)
+        seen += 1
+    assert seen == 8, seen   # d in {64, 128} x causal x block mask
