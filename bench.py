@@ -206,12 +206,17 @@ def cpu_baseline(w, q, k, v, do, bm, seconds: float):
     fdone, fdt = run(False, seconds / 2, done)
     rho = kept_fraction(w.N, w.causal, bm)
     fwd_head = 4.0 * w.N * w.N * w.d * rho
+    # what the oracle executes: dense products over every (query, key) pair, masked
+    # ones included: S and P V (4 N^2 d), then dV, dP, dQ, dK (8 N^2 d)
+    exe_fwd, exe_all = 4.0 * w.N * w.N * w.d, 12.0 * w.N * w.N * w.d
     return {"value": 3.5 * fwd_head * done / dt / 1e12, "unit": "TFLOP/s",
+            "executed_tflops": exe_all * done / dt / 1e12,
             "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {w.B * w.H} heads of {w.name}, forward+backward, fp64 "
                       f"NumPy with S and P materialised, {dt:.2f} s",
             "seconds": dt,
             "fwd": {"value": fwd_head * fdone / fdt / 1e12, "unit": "TFLOP/s",
+                    "executed_tflops": exe_fwd * fdone / fdt / 1e12,
                     "sample": f"{fdone} heads, forward only, {fdt:.2f} s", "seconds": fdt},
             "cpu": cpu_model(), "host_cpus": os.cpu_count()}
 

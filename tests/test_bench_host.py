@@ -8,6 +8,7 @@ traffic records it reads from profiles/, and its one-GPU guard.
   hand, pass by pass, at the causal8k shape (the figure quoted in the profiles).
 * Each committed traffic record must be consistent with its own raw counter
   values and calibration factors.
+* The CPU oracle timing reports both the algorithmic and the executed rate.
 """
 import json
 import os
@@ -108,3 +109,17 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_reports_algorithmic_and_executed_rates():
+    """The oracle timing on the tiny causal shape: algorithmic TFLOP/s counts
+    3.5 x 4 N^2 d rho per head, executed TFLOP/s the 12 N^2 d the materialising
+    oracle runs; their ratio is fixed by the shape."""
+    from exact_io_aware_61_amd.workloads import WORKLOADS, kept_fraction, make_inputs, variant
+    w = variant(WORKLOADS["tiny"], causal=True)
+    q, k, v, do, bm = make_inputs(w)
+    cb = bench.cpu_baseline(w, q, k, v, do, bm, seconds=0.05)
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["cores"] >= 1
+    rho = kept_fraction(w.N, w.causal, bm)
+    assert cb["executed_tflops"] / cb["value"] == pytest.approx(12.0 / (14.0 * rho))
+    assert cb["fwd"]["executed_tflops"] / cb["fwd"]["value"] == pytest.approx(1.0 / rho)
