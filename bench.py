@@ -395,6 +395,55 @@ def fwd_rows_per_workgroup(d: int, masked: bool) -> int:
     return 128 if (masked or d == 64) else 256
 
 
+def pass_io_models(N: int, d: int, causal: bool, block_mask, heads: int) -> dict:
+    """Device bytes of each pass of the step per launch: compulsory (every tensor read or
+    written once) and the tile model (the Theta(N^2 d^2 / M) term: the streamed operand
+    re-read once for every workgroup that visits it), counted from the kernels' loops.
+
+    Forward and dQ: a workgroup per block of BM query rows streams the K/V tiles of 64
+    keys (32 for the unmasked d=64 dQ) it sees. dK/dV: a workgroup per block of 128 keys
+    streams the Q/dO tiles of 64 rows (plus their D and L2 rows, 8 bytes per row) it
+    sees. Preprocess: O and dO read, LSE read, D and L2 written. A tile is visited if
+    one of its (query, key) pairs is attended (causal: key <= query; block mask: its
+    128 x 128 block kept). block_mask: [ceil(N/128)]^2 array or None.
+    """
+    import numpy as np
+    nb = -(-N // 128)
+    keep = np.ones((nb, nb), bool) if block_mask is None else np.asarray(block_mask).astype(bool)
+    masked = block_mask is not None
+
+    def visits(rows, keys):
+        """(row block, key block) pairs with an attended pair; rows, keys: block sizes,
+        keys <= 128 and dividing 128, so a key block lies inside one mask column."""
+        nk = -(-N // keys)
+        col = (np.arange(nk) * keys) // 128          # mask column of each key block
+        total = 0
+        for r0 in range(0, N, rows):
+            r1 = min(N, r0 + rows) - 1
+            seen = keep[r0 // 128:r1 // 128 + 1].any(axis=0)[col]   # kept in any of its mask rows
+            upto = r1 // keys + 1 if causal else nk                 # causal: keys <= last row
+            total += int(seen[:upto].sum())
+        return total
+
+    nd = N * d
+    bm_fwd = fwd_rows_per_workgroup(d, masked)
+    bm_dq = 128 if (masked or d == 64) else 256
+    bn_dq = 32 if (d == 64 and not masked) else 64
+    v_fwd, v_dq, v_kv = visits(bm_fwd, 64), visits(bm_dq, bn_dq), visits(64, 128)
+    per_head = {
+        "compulsory_fwd": 8 * nd + 4 * N,
+        "tile_model_fwd": 4 * nd + v_fwd * 64 * d * 4 + 4 * N,
+        "compulsory_pre": 4 * nd + 12 * N,
+        "compulsory_dkdv": 12 * nd + 8 * N,
+        "tile_model_dkdv": 8 * nd + v_kv * (64 * d * 4 + 64 * 8),
+        "compulsory_dq": 10 * nd + 8 * N,
+        "tile_model_dq": 6 * nd + 8 * N + v_dq * bn_dq * d * 4,
+    }
+    out = {k: heads * v for k, v in per_head.items()}
+    out["rows_per_workgroup_fwd"] = bm_fwd
+    return out
+
+
 def kv_outer_io_model(N: int, d: int, causal: bool, heads: int) -> float:
     """Device bytes of the K/V-outer forward per launch, counted from its loops.
 
@@ -728,17 +777,11 @@ def main():
                 "traffic": None if rec is None else rec["bytes_per_launch"],
                 "avg_launch_ms": round(per[dom], 4), "flop_per_launch": kernel_flop[dom]}
 
-    # Forward IO accounting in bytes (per launch): the compulsory traffic (Q, K, V
-    # read and O written once, LSE written), and the tile model of the tiled
-    # forward, where every block of BR query rows re-reads the K and V tiles it
-    # attends (4*N*d*ceil(N/BR)*rho per head: the Theta(N^2 d^2 / M) term) on top
-    # of reading Q and writing O once. BR is the forward's rows per workgroup.
-    br = fwd_rows_per_workgroup(w.d, bm is not None)
+    # IO accounting in bytes per launch of each pass: the compulsory traffic (every
+    # tensor read or written once) and the tile model (the streamed operand re-read
+    # by every workgroup that visits it: the Theta(N^2 d^2 / M) term).
     heads = w.B * w.H
-    io = {"compulsory_fwd": heads * (8 * w.N * w.d + 4 * w.N),
-          "tile_model_fwd": heads * (4 * w.N * w.d + 4 * w.N * w.d * (-(-w.N // br)) * rho
-                                     + 4 * w.N),
-          "rows_per_workgroup_fwd": br}
+    io = pass_io_models(w.N, w.d, w.causal, bm, heads)
 
     fwd_tf = fwd_flop / (fwd_ms * 1e-3) / 1e12
     fb_ms = fwd_ms + bwd_ms

@@ -9,6 +9,8 @@ traffic records it reads from profiles/, and its one-GPU guard.
 * Each committed traffic record must be consistent with its own raw counter
   values and calibration factors.
 * The CPU oracle timing reports both the algorithmic and the executed rate.
+* pass_io_models' tile visits are checked against a walk over every (query, key)
+  pair of small ragged shapes.
 """
 import json
 import os
@@ -123,3 +125,42 @@ def test_cpu_baseline_reports_algorithmic_and_executed_rates():
     rho = kept_fraction(w.N, w.causal, bm)
     assert cb["executed_tflops"] / cb["value"] == pytest.approx(12.0 / (14.0 * rho))
     assert cb["fwd"]["executed_tflops"] / cb["fwd"]["value"] == pytest.approx(1.0 / rho)
+
+
+def _visits_by_pairs(N, rows, keys, causal, keep):
+    """Blocks of `rows` query rows x `keys` keys holding at least one attended pair,
+    found by testing the pairs one by one."""
+    import numpy as np
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    att = keep[i // 128, j // 128] & ((j <= i) if causal else True)
+    total = 0
+    for r0 in range(0, N, rows):
+        for k0 in range(0, N, keys):
+            total += bool(att[r0:r0 + rows, k0:k0 + keys].any())
+    return total
+
+
+@pytest.mark.parametrize("N,d,causal,masked", [(300, 64, True, False), (300, 128, False, False),
+                                               (640, 64, False, True), (640, 128, True, True),
+                                               (1, 64, True, False)])
+def test_pass_io_models_match_pair_walk(N, d, causal, masked):
+    import numpy as np
+    nb = -(-N // 128)
+    rng = np.random.default_rng(N + d)
+    mask = (rng.random((nb, nb)) < 0.4) | np.eye(nb, dtype=bool) if masked else None
+    keep = np.ones((nb, nb), bool) if mask is None else mask
+    io = bench.pass_io_models(N, d, causal, mask, heads=3)
+    bm_fwd = bench.fwd_rows_per_workgroup(d, masked)
+    bm_dq = 128 if (masked or d == 64) else 256
+    bn_dq = 32 if (d == 64 and not masked) else 64
+    nd = N * d
+    assert io["tile_model_fwd"] == 3 * (4 * nd + 4 * N
+                                        + _visits_by_pairs(N, bm_fwd, 64, causal, keep) * 64 * d * 4)
+    assert io["tile_model_dq"] == 3 * (6 * nd + 8 * N
+                                       + _visits_by_pairs(N, bm_dq, bn_dq, causal, keep) * bn_dq * d * 4)
+    assert io["tile_model_dkdv"] == 3 * (8 * nd
+                                         + _visits_by_pairs(N, 64, 128, causal, keep) * (64 * d * 4 + 512))
+    assert io["compulsory_fwd"] == 3 * (8 * nd + 4 * N)
+    assert io["compulsory_dkdv"] == 3 * (12 * nd + 8 * N)
+    assert io["compulsory_dq"] == 3 * (10 * nd + 8 * N)
