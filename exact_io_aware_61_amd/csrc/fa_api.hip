@@ -10,6 +10,8 @@
 namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+// A dispatch counts its work-items in 32 bits: every launch stays below 2^32.
+constexpr int64_t kMaxWorkItems = (int64_t(1) << 32) - 1;
 // Sequence lengths stay this far below 2^31 so that rounding N up to any tile
 // (at most 256 rows) stays inside int.
 constexpr int kMaxSeq = INT32_MAX - 1024;
@@ -28,6 +30,11 @@ int check_shape(const Shape& s) {
   // B*H*N*d can exceed 2^63 before the limit check (B*H and N up to 2^31 - 1 each)
   if ((unsigned __int128)s.bh() * (unsigned)s.N * (unsigned)s.d >= (unsigned __int128)kMaxElems)
     return FA_ERR_SHAPE;
+  // The widest launches (the backward preprocess, dK/dV at d = 128) run four
+  // work-items per row of every head, rows rounded up to the 256-row blocks of
+  // the forward; the other attention launches run at most two per row, and the
+  // K/V-outer forward 256 per head. B*H*N < 2^34 here, so this cannot overflow.
+  if (4 * s.bh() * (((int64_t)s.N + 255) / 256 * 256) > kMaxWorkItems) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -161,6 +168,10 @@ int decode_shape(int B, int H, int Nq, int Nk, int d) {
   if ((unsigned __int128)((int64_t)B * H) * (uint64_t)((int64_t)Nk + Nq) * (unsigned)d >=
       (unsigned __int128)kMaxElems)
     return FA_ERR_SHAPE;
+  // Work-items of the two launches: the merge runs d per query row of every
+  // head, the key split 64 per chunk, with at most B*H + 1024 chunks in all.
+  const int64_t bh = (int64_t)B * H;
+  if (bh * Nq * d > kMaxWorkItems || 64 * (bh + 1024) > kMaxWorkItems) return FA_ERR_SHAPE;
   return FA_OK;
 }
 size_t decode_ws_o(int64_t BH, int Nq, int Nk, int d) {
@@ -187,7 +198,9 @@ const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "unsupported shape: need B, H, N >= 0, d in {64, 128}, B*H*N*d < 2^40";
+    case FA_ERR_SHAPE:
+      return "unsupported shape: need B, H, N >= 0, d in {64, 128}, B*H*N*d < 2^40, and at most "
+             "2^32 - 1 work-items per launch";
     case FA_ERR_MASK: return "invalid mask: unknown kind, block != 128, or missing block grid";
     case FA_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
     case FA_ERR_WORKSPACE: return "backward workspace missing or smaller than fa_bwd_workspace_size()";

@@ -28,7 +28,9 @@
  *   Alignment  data pointers must be 16-byte aligned.
  *   Limits     B, H, N >= 0 (a zero extent is a no-op that returns FA_OK);
  *              d in {64, 128}; scale finite and > 0; B*H*N*d < 2^40;
- *              N <= 2^31 - 1025 (B*H <= 2^31 - 1 follows).
+ *              N <= 2^31 - 1025 (B*H <= 2^31 - 1 follows);
+ *              4*B*H*ceil(N / 256)*256 <= 2^32 - 1, so that no launch asks
+ *              for 2^32 work-items or more (a dispatch counts them in 32 bits).
  *              N need not be a multiple of any tile size. With a block mask,
  *              ceil(N / 128) <= 16384 (N <= 2^21).
  *   Streams    `stream` is a hipStream_t passed as void* (NULL = default
@@ -185,7 +187,9 @@ int fa_fwd_kv_outer(const void* q, const void* k, const void* v, void* o, float*
  *   workspace : DEVICE buffer of at least fa_decode_workspace_size() bytes,
  *               caller-owned, contents irrelevant on entry, overwritten
  * Limits: 0 <= Nq <= 32, 0 <= Nk <= 2^31 - 1025 (k and v may be NULL when Nk = 0),
- * d in {64, 128}, B*H*(Nq+Nk)*d < 2^40. Errors and streams as above; outputs
+ * d in {64, 128}, B*H*(Nq+Nk)*d < 2^40, B*H*Nq*d <= 2^32 - 1 and
+ * 64*(B*H + 1024) <= 2^32 - 1 (work-items of the merge and the key split).
+ * Errors and streams as above; outputs
  * and workspace must not overlap each other or any input.
  */
 int fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, size_t* bytes);

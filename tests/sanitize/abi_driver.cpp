@@ -134,7 +134,13 @@ void forward_checks() {
          FA_ERR_SHAPE);   // N past 2^31 - 1025
   EXPECT(fa_fwd(q.p, k.p, v.p, o.p, (float*)lse.p, 1, 1, 0x7fffffff - 1024, 128, sc, nullptr,
                 nullptr),
-         FA_ERR_ALIAS);   // a legal size, but then these buffers overlap
+         FA_ERR_SHAPE);   // under 2^40 elements, but a launch would need 2^33 work-items
+  EXPECT(fa_fwd(q.p, k.p, v.p, o.p, (float*)lse.p, 1, 1, (1 << 30) - 255, 128, sc, nullptr,
+                nullptr),
+         FA_ERR_SHAPE);   // 4 * 2^30 work-items: one past the limit
+  EXPECT(fa_fwd(q.p, k.p, v.p, o.p, (float*)lse.p, 1, 1, (1 << 30) - 256, 128, sc, nullptr,
+                nullptr),
+         FA_ERR_ALIAS);   // the largest legal N for one head, but then these buffers overlap
 }
 
 void backward_checks() {

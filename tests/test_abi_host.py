@@ -82,6 +82,10 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, d=256) == SHAPE
     assert fwd(lib, N=-1) == SHAPE
     assert fwd(lib, B=1 << 20, H=1 << 20, N=1 << 10, d=64) == SHAPE   # > 2^40 elements
+    # under 2^40 elements, but 4*B*H*ceil(N/256)*256 work-items reach 2^32
+    assert fwd(lib, B=1, H=1 << 21, N=512, d=64) == SHAPE
+    assert fwd(lib, B=1, H=1 << 21, N=257, d=64) == SHAPE
+    assert fwd(lib, q=None, B=1, H=(1 << 21) - 1, N=512, d=64) == NULL   # just inside
     assert fwd(lib, scale=0.0) == SCALE
     assert fwd(lib, scale=float("nan")) == SCALE
     assert fwd(lib, scale=float("inf")) == SCALE
@@ -173,6 +177,12 @@ def test_decode_rejects_bad_arguments(lib):
     need = n.value   # placeholder buffers 64 KiB apart: keep the shapes below that size
     assert lib.fa_decode_workspace_size(2, 4, 33, 4096, 128, ctypes.byref(n)) == SHAPE
     assert lib.fa_decode_workspace_size(2, 4, 8, 4096, 96, ctypes.byref(n)) == SHAPE
+    # work-items per launch stay below 2^32: the merge runs B*H*Nq*d of them,
+    # the key split 64 per chunk with up to B*H + 1024 chunks
+    assert lib.fa_decode_workspace_size(1, 1 << 20, 32, 1, 128, ctypes.byref(n)) == SHAPE
+    assert lib.fa_decode_workspace_size(1, (1 << 20) - 1, 32, 1, 128, ctypes.byref(n)) == OK
+    assert lib.fa_decode_workspace_size(1, (1 << 26) - 1024, 1, 1, 64, ctypes.byref(n)) == SHAPE
+    assert lib.fa_decode_workspace_size(1, (1 << 26) - 1025, 1, 1, 64, ctypes.byref(n)) == OK
     ws = P[11]
 
     def dec(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], Nq=16, Nk=64, d=128, scale=0.1,
