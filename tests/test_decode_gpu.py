@@ -61,6 +61,39 @@ def test_decode_parity(B, H, Nq, Nk, d, causal):
     _compare(o, lse, ref)
 
 
+@pytest.mark.parametrize("Nk", [31, 32, 33, 255, 256, 257, 511])
+@pytest.mark.parametrize("Nq", [1, 31, 32])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_chunk_edges(Nk, Nq, causal):
+    """Cache lengths on and next to the 32-key tile and the 256-key smallest chunk, with one,
+    31 and 32 queries (with the causal mask and Nq > Nk the first rows see no key)."""
+    B, H, d = 1, 2, 128
+    q, k, v = _inputs(B, H, Nq, Nk, d, seed=700 + Nq + Nk)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    print(f"[case] decode chunk edge Nq={Nq} Nk={Nk} causal={causal}", flush=True)
+    o, lse = fa.decode(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref = decode_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale=scale,
+                     causal=causal)
+    _compare(o, lse, ref)
+
+
+@pytest.mark.parametrize("Nk", [8191, 8193])
+def test_decode_many_chunks_ragged_last(Nk):
+    """One head, so about 1024 chunks are wanted and the cache length sets them (chunks of at
+    least 256 keys): 8191 keys make 32 chunks of 256, the last one key short; 8193 make 33
+    chunks of 256, the last holding a single key."""
+    B, H, Nq, d = 1, 1, 8, 64
+    q, k, v = _inputs(B, H, Nq, Nk, d, seed=800 + Nk)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    print(f"[case] decode many chunks Nk={Nk}", flush=True)
+    o, lse = fa.decode(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    ref = decode_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale=scale,
+                     causal=True)
+    _compare(o, lse, ref)
+
+
 def test_decode_square_matches_training_forward():
     """Nq = Nk with the causal mask is the training forward (top-left = bottom-right)."""
     q, k, v = _inputs(1, 2, 32, 32, 128, seed=91)
