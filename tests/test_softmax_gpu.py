@@ -55,6 +55,19 @@ def test_softmax_rows_parity(rows, cols, sigma):
     _check(y, x.astype(np.float64))
 
 
+@pytest.mark.parametrize("cols", [252, 256, 258, 260, 512, 516, 1024, 1028, 2048, 2052, 4092])
+def test_softmax_rows_kernel_switch_points(cols):
+    """Rows of 16-byte-aligned floats up to 4096 run the register kernel, one wave per row
+    holding 4, 8, 16, 32 or 64 floats per lane (row lengths up to 256, 512, 1024, 2048,
+    4096); other lengths run the streaming kernel. Lengths on and next to each switch point,
+    one that is not a multiple of four (258) among them."""
+    x = _inputs(11, cols, 4.0, seed=5000 + cols)
+    print(f"[case] softmax switch point cols={cols}", flush=True)
+    y = fa.softmax_rows(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    _check(y, x.astype(np.float64))
+
+
 def test_softmax_rows_in_place_and_unaligned():
     x = _inputs(17, 2048, 4.0, seed=3)
     print("[case] softmax in place", flush=True)
