@@ -30,7 +30,7 @@ def _check(o, lse, ref, sel=(slice(None),)):
     assert np.max(np.abs(lse - ref["lse"][sel])) <= 1e-3
 
 
-@pytest.mark.parametrize("N", [1, 65, 200, 333])
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 127, 128, 129, 200, 256, 257, 333])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_kv_outer_parity(N, d, causal):
