@@ -21,6 +21,13 @@ def pytest_collection_modifyitems(config, items):
     except Exception:  # pragma: no cover
         has_gpu = False
     if has_gpu:
+        # A GPU test that stops making progress ends the run instead of holding the
+        # GPU: 600 s each (the whole GPU suite takes a minute or two), interrupted
+        # from a watchdog thread, since a test stuck in a GPU call cannot be
+        # interrupted by a signal.
+        for item in items:
+            if "gpu" in item.keywords and item.get_closest_marker("timeout") is None:
+                item.add_marker(pytest.mark.timeout(600, method="thread"))
         return
     skip = pytest.mark.skip(reason="no GPU visible")
     for item in items:
