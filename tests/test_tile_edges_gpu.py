@@ -72,3 +72,26 @@ def test_peaked_scores(d, causal):
     gpu = run_gpu(q, k, v, do, causal=causal, scale=_scale(d))
     ref = run_oracle(q, k, v, do, causal=causal, scale=_scale(d))
     assert_parity(gpu, ref, label=f"peaked d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,masked", [(16, 64, 96, 64, True, False),
+                                                    (8, 128, 130, 128, False, True),
+                                                    (7, 9, 300, 128, True, True),
+                                                    (9, 7, 257, 64, False, True)])
+def test_many_heads_and_head_orders(B, H, N, d, causal, masked):
+    """Many heads with few row blocks each (1024 heads), and B*H = 63, which is not a
+    multiple of 8, so masked launches keep the interleaved workgroup order instead of
+    the head-major one; block masks are per head. Every head is compared in full."""
+    q, k, v, do = make_qkv(B, H, N, d, seed=9950 + B * H + N)
+    bm = None
+    if masked:
+        nb = -(-N // 128)
+        rng = np.random.default_rng(9960 + N)
+        bm = (rng.random((B, H, nb, nb)) < 0.6).astype(np.uint8)
+        for b in range(B):
+            for h in range(H):
+                np.fill_diagonal(bm[b, h], 1)
+    print(f"[case] many heads B={B} H={H} N={N} d={d} causal={causal} masked={masked}", flush=True)
+    gpu = run_gpu(q, k, v, do, causal=causal, block_mask=bm, scale=_scale(d))
+    ref = run_oracle(q, k, v, do, causal=causal, block_mask=bm, scale=_scale(d))
+    assert_parity(gpu, ref, label=f"many heads B={B} H={H} N={N} d={d}")
