@@ -107,3 +107,22 @@ def test_forward_rows_per_workgroup_match_bench_model(asm):
         assert rows == bench.fwd_rows_per_workgroup(d, block), (name, threads)
         seen += 1
     assert seen == 8, seen   # d in {64, 128} x causal x block mask
+
+
+def test_no_bit_cast_of_a_vector_element():
+    """`__builtin_bit_cast(T, v[i])` on an element of an ext_vector_type vector compiles, with
+    this hipcc, to a read of element 0 whatever i is (a kernel that summed four packed pairs
+    this way read the first pair four times). The kernels copy such an element into a scalar
+    before casting it; this keeps the construct out of the sources."""
+    import re
+    pat = re.compile(r"__builtin_bit_cast\(\s*[\w:]+\s*,\s*[\w.]+(\s*\[[^\]]+\])+\s*\)")
+    csrc = fab.CSRC
+    bad = []
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            for n, line in enumerate(open(os.path.join(csrc, name)), 1):
+                if pat.search(line):
+                    bad.append(f"{name}:{n}: {line.strip()}")
+    assert not bad, bad
+    assert pat.search("x = __builtin_bit_cast(bf16x2, pku[k][h]);")      # the pattern works
+    assert not pat.search("x = __builtin_bit_cast(bf16x8, v);")
